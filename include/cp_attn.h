@@ -1,0 +1,187 @@
+/*
+ * cp_attn.h -- causal ring attention, one context-parallel rank's share, on
+ * AMD MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [MLM] "Megatron-LM源码解析：Context Parallel如何革新长序列训练"
+ *         (mieleap.com/news/151524), sections 1-6.
+ *   [RAF] "如何用Context并行加速大模型训练？手把手教你配置RingAttention+FlashAttention"
+ *         (devpress.csdn.net), sections 1-5.
+ *
+ * The operation.  A rank holds a local block of queries and, over the steps of
+ * a ring, receives the K/V blocks of the other ranks ([RAF] section 3: the
+ * RingAttention loop; at step j rank r uses the block of rank (r - j) mod N).
+ * For every local query at absolute position i it computes causal softmax
+ * attention over every key at position j <= i ([RAF] section 1; [RAF] section
+ * 3, note 2: the mask comes from the blocks' absolute offsets):
+ *
+ *     LSE_i = ln sum_{j<=i} exp(tau <q_i,k_j>),   out_i = sum_{j<=i} exp(tau <q_i,k_j> - LSE_i) v_j
+ *
+ * Each ring step yields a partial (O, LSE) over its key block; partials are
+ * combined by log-sum-exp rescaling (the exact rule behind the page's
+ * simplified "add the chunk outputs" in [RAF] section 3, step 5).
+ * Sharding uses the 2N zigzag split of [RAF] section 5, item 1.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense, contiguous, row-major [B, H, S, D] (D fastest),
+ *     device pointers, 16-byte aligned.  Q/K/V/out are bf16 (raw 16-bit
+ *     storage, passed as void*); O and LSE accumulators are fp32.
+ *   - A "local" buffer of S tokens is n_chunks chunks of chunk_len tokens,
+ *     concatenated in order; cp_chunks_t.start[i] is the absolute position of
+ *     the first token of chunk i in the full sequence.
+ *   - LSE is the natural-log sum of exp(tau * q.k); -INFINITY marks a row
+ *     that has no visible key (its O is 0).
+ *   - Ownership: the caller owns every device buffer, including workspace.
+ *     The library never allocates device memory.  Host arrays and structs are
+ *     read only during the call.
+ *   - Asynchrony: calls only enqueue work on the given stream(s); inputs must
+ *     stay valid until that work has run.  Kernel faults surface at the
+ *     caller's next synchronisation.
+ *   - Errors: arguments are checked before anything is enqueued.  A non-OK
+ *     status leaves every output untouched and sets a thread-local message
+ *     readable with cp_last_error().  No C++ exception crosses the ABI.
+ *   - Thread safety: the library keeps a per-device pool of HIP events for the
+ *     ring driver; calls are not re-entrant from several host threads on the
+ *     same device.
+ */
+#ifndef CP_ATTN_H
+#define CP_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CP_MAX_CHUNKS 8
+#define CP_MAX_STEPS 64
+
+/* Chunk table of a local buffer: n_chunks (1..CP_MAX_CHUNKS) chunks of
+ * chunk_len tokens each (chunk_len > 0 and a multiple of 64); start[i] >= 0
+ * is the absolute position of chunk i.  Chunks must not overlap. */
+typedef struct {
+    int32_t n_chunks;
+    int32_t chunk_len;
+    int64_t start[CP_MAX_CHUNKS];
+} cp_chunks_t;
+
+typedef enum {
+    CP_OK = 0,
+    CP_ERR_INVALID = 1,      /* bad argument (message in cp_last_error) */
+    CP_ERR_UNSUPPORTED = 2,  /* valid but not built (e.g. head dim) */
+    CP_ERR_WORKSPACE = 3,    /* workspace too small */
+    CP_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+} cp_status_t;
+
+enum { CP_STEP_WRITE = 0, CP_STEP_MERGE = 1 };
+
+/* Text describing the last non-OK status returned on this host thread. */
+const char* cp_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int cp_version(void);
+
+/*
+ * Zigzag shard and ring schedule ([RAF] section 5 item 1; [RAF] section 3).
+ * The full sequence is cut into 2*cp_size chunks of chunk_len tokens; rank r
+ * holds chunks r and 2*cp_size-1-r (ascending).  At ring step `step` the rank
+ * works on the K/V block of rank (rank - step) mod cp_size.
+ * Writes the query table of `rank` to *q_chunks and the K/V table of that
+ * step's source rank to *kv_chunks (either pointer may be NULL).
+ * Errors: CP_ERR_INVALID if cp_size < 1, rank or step outside [0, cp_size),
+ * or chunk_len <= 0.
+ */
+cp_status_t cp_zigzag_chunks(int cp_size, int rank, int chunk_len, int step,
+                             cp_chunks_t* q_chunks, cp_chunks_t* kv_chunks);
+
+/*
+ * One ring step: partial causal attention of the local queries against one
+ * K/V block, merged into running fp32 accumulators (the per-step fused
+ * attention call of [MLM] section 5 and [RAF] section 3, step 4, with the
+ * log-sum-exp merge in place of the page's plain sum).
+ *
+ *   q   bf16 [B,H,Sq,D],  Sq  = q_chunks->n_chunks  * q_chunks->chunk_len
+ *   k,v bf16 [B,H,Skv,D], Skv = kv_chunks->n_chunks * kv_chunks->chunk_len
+ *   o   fp32 [B,H,Sq,D] running output (normalised), lse fp32 [B,H,Sq]
+ *   out_bf16_or_null  bf16 [B,H,Sq,D]: if non-NULL, also write bf16(o) (RNE)
+ *   mode CP_STEP_WRITE: (o,lse) := partial of this block (rows with no
+ *        visible key get o = 0, lse = -inf);
+ *        CP_STEP_MERGE: (o,lse) := merge((o,lse), partial); rows with no
+ *        visible key keep their values.
+ *   softmax_scale > 0 and finite (1/sqrt(D) for the standard definition).
+ * Supported: D in {64, 128}; B, H >= 1.  q, k, v must not alias o/lse/out.
+ */
+cp_status_t cp_attn_step_fwd(const void* q, const void* k, const void* v,
+                             float* o, float* lse, void* out_bf16_or_null,
+                             int B, int H, int D,
+                             const cp_chunks_t* q_chunks, const cp_chunks_t* kv_chunks,
+                             float softmax_scale, int mode, hipStream_t stream);
+
+/*
+ * Standalone log-sum-exp merge of two partial results, in place on the
+ * accumulator: L = ln(e^La + e^Lb), O = e^(La-L) Oa + e^(Lb-L) Ob; an
+ * operand with LSE = -inf contributes nothing; both empty gives (0, -inf).
+ *   o_acc, o_part fp32 [B,H,Sq,D]; lse_acc, lse_part fp32 [B,H,Sq]
+ *   out_bf16_or_null: if non-NULL, also write bf16 of the merged O.
+ * Supported: D a multiple of 4 (any size), Sq >= 0.
+ */
+cp_status_t cp_attn_merge(float* o_acc, float* lse_acc,
+                          const float* o_part, const float* lse_part,
+                          int B, int H, int Sq, int D, void* out_bf16_or_null,
+                          hipStream_t stream);
+
+/* Workspace bytes cp_ring_attn_fwd needs: two staging slots for one K and one
+ * V block [B,H,Skv,D] bf16, plus the fp32 running output [B,H,Sq,D],
+ * each rounded up to 256 bytes.  Returns 0 for non-positive sizes. */
+size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq);
+
+/*
+ * A rank's whole share of causal ring attention, replayed on one GPU.
+ *   q         bf16 [B,H,Sq,D] with table *q_chunks
+ *   k_steps[j], v_steps[j]  host array of n_steps device pointers, ring order:
+ *             the K/V block the rank uses at step j, bf16 [B,H,Skv,D], with
+ *             table kv_chunks_steps[j] (all the same chunk_len and count).
+ *             Step 0 is read in place (the rank's own block); for j >= 1 the
+ *             block is first copied into one of two staging slots in the
+ *             workspace on copy_stream, standing in for the peer-to-peer
+ *             receive ([MLM] section 5: double buffering on a separate
+ *             stream; [RAF] section 3: receive from the previous rank).
+ *   out       bf16 [B,H,Sq,D], lse fp32 [B,H,Sq]  (final results)
+ *   workspace at least cp_ring_attn_workspace_bytes(B,H,Skv,D,Sq) bytes,
+ *             256-byte aligned.
+ *   copy_stream  a stream other than `stream` (not NULL).
+ * The copy of step j+1 overlaps the compute of step j; the copy into a slot
+ * waits until the step that last read that slot has finished.  On entry
+ * copy_stream waits for prior work on `stream`; before returning, `stream`
+ * waits for every copy, so later work on `stream` is ordered after the call.
+ * Every query row must see at least one key over the steps (true for a
+ * zigzag share, whose step 0 contains the diagonal).
+ * Errors: CP_ERR_INVALID for bad tables or n_steps outside [1, CP_MAX_STEPS],
+ * CP_ERR_WORKSPACE if workspace_bytes is too small.
+ */
+cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks,
+                             const void* const* k_steps, const void* const* v_steps,
+                             const cp_chunks_t* kv_chunks_steps, int n_steps,
+                             void* out, float* lse,
+                             int B, int H, int D, float softmax_scale,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, hipStream_t copy_stream);
+
+/*
+ * Kernel timing for measurement.  While enabled, every attention-step kernel
+ * launched by cp_attn_step_fwd / cp_ring_attn_fwd is bracketed by two HIP
+ * events on its stream.  cp_profile_read waits for those events, writes up to
+ * max_entries elapsed times (milliseconds, launch order) to kernel_ms and
+ * their count to *n_entries, and clears the record.  At most 4096 launches
+ * are kept; later ones are not timed.  Enabling or disabling clears the record.
+ */
+cp_status_t cp_profile_enable(int enable);
+cp_status_t cp_profile_read(float* kernel_ms, int max_entries, int* n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_ATTN_H */

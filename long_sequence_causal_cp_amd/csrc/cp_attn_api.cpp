@@ -1,0 +1,438 @@
+// C ABI of the causal ring-attention library: argument checks, per-step work
+// planning, the one-GPU ring replay (staging slots, side stream, events) and
+// kernel timing.  See include/cp_attn.h for the contract of each entry point.
+//
+// Sources (web pages, cited by title and section):
+//   [MLM] "Megatron-LM源码解析：Context Parallel如何革新长序列训练", section 5
+//         (double-buffered loop of cp_size+1 iterations: while step i computes
+//         on buffer i%2, the transfer for step i+1 fills the other buffer on
+//         its own stream) and section 3 (the context-parallel work runs on a
+//         dedicated stream).
+//   [RAF] "如何用Context并行加速大模型训练？手把手教你配置RingAttention+FlashAttention",
+//         section 3 (ring order: step j uses the block of rank (rank - j) mod N)
+//         and section 5, item 1 (2N zigzag chunks).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/cp_attn.h"
+#include "cp_attn_internal.h"
+
+using cpattn::StepArgs;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cp_status_t fail(cp_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+cp_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(CP_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+cp_status_t check_chunks(const cp_chunks_t* t, const char* name) {
+  if (!t) return fail(CP_ERR_INVALID, "%s is NULL", name);
+  if (t->n_chunks < 1 || t->n_chunks > CP_MAX_CHUNKS)
+    return fail(CP_ERR_INVALID, "%s.n_chunks = %d, must be in [1, %d]", name, t->n_chunks, CP_MAX_CHUNKS);
+  if (t->chunk_len <= 0 || t->chunk_len % 64 != 0)
+    return fail(CP_ERR_INVALID, "%s.chunk_len = %d, must be a positive multiple of 64", name, t->chunk_len);
+  for (int i = 0; i < t->n_chunks; ++i) {
+    if (t->start[i] < 0 || t->start[i] > (int64_t)INT32_MAX - t->chunk_len)
+      return fail(CP_ERR_INVALID, "%s.start[%d] = %lld out of range [0, 2^31 - chunk_len]", name, i,
+                  (long long)t->start[i]);
+    for (int j = 0; j < i; ++j)
+      if (t->start[i] < t->start[j] + t->chunk_len && t->start[j] < t->start[i] + t->chunk_len)
+        return fail(CP_ERR_INVALID, "%s: chunks %d and %d overlap", name, j, i);
+  }
+  return CP_OK;
+}
+
+cp_status_t check_common(int B, int H, int D, float scale) {
+  if (B < 1 || H < 1) return fail(CP_ERR_INVALID, "B = %d and H = %d must be >= 1", B, H);
+  if ((long long)B * H > (1LL << 24)) return fail(CP_ERR_INVALID, "B*H = %lld too large", (long long)B * H);
+  if (D != 64 && D != 128) return fail(CP_ERR_UNSUPPORTED, "head dim D = %d not built (64 or 128)", D);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(CP_ERR_INVALID, "softmax_scale = %g must be finite and > 0", (double)scale);
+  return CP_OK;
+}
+
+// Visible (query, key) pairs between a query chunk starting at qs and a key
+// chunk starting at ks (key position <= query position).
+long long chunk_pairs(long long qs, long long lq, long long ks, long long lk) {
+  auto S = [lk](long long n) -> long long {  // sum_{x=1..n} min(x, lk), n >= 0
+    if (n <= 0) return 0;
+    if (n <= lk) return n * (n + 1) / 2;
+    return lk * (lk + 1) / 2 + (n - lk) * lk;
+  };
+  const long long a = qs - ks + 1, b = qs - ks + lq;
+  return S(b) - S(a - 1);
+}
+
+long long pairs_for_chunk(const cp_chunks_t* q, int c, const cp_chunks_t* kv) {
+  long long p = 0;
+  for (int j = 0; j < kv->n_chunks; ++j) p += chunk_pairs(q->start[c], q->chunk_len, kv->start[j], kv->chunk_len);
+  return p;
+}
+
+// Fill the launch arguments shared by every step; flags/order set by caller.
+void base_args(StepArgs& a, const void* q, const void* k, const void* v, float* o, float* lse, void* out,
+               int B, int H, const cp_chunks_t* qc, const cp_chunks_t* kvc, float scale) {
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o_run = o;
+  a.lse_run = lse;
+  a.out = static_cast<uint16_t*>(out);
+  a.BH = B * H;
+  a.Sq = qc->n_chunks * qc->chunk_len;
+  a.Skv = kvc->n_chunks * kvc->chunk_len;
+  a.q_chunk_len = qc->chunk_len;
+  a.kv_chunk_len = kvc->chunk_len;
+  a.n_kv_chunks = kvc->n_chunks;
+  for (int i = 0; i < qc->n_chunks; ++i) a.q_start[i] = (int)qc->start[i];
+  for (int i = 0; i < kvc->n_chunks; ++i) a.kv_start[i] = (int)kvc->start[i];
+  a.rb_per_chunk = qc->chunk_len / cpattn::step_block_rows(qc->chunk_len);
+  a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+}
+
+// Order the active query chunks heaviest first so long-running workgroups start early.
+void set_order(StepArgs& a, const std::vector<int>& active, const std::vector<long long>& work) {
+  std::vector<int> idx(active);
+  std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return work[x] > work[y]; });
+  a.n_order = (int)idx.size();
+  for (int i = 0; i < a.n_order; ++i) a.order[i] = idx[i];
+}
+
+// ---------------- kernel timing ----------------
+struct Profiler {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  size_t used = 0;
+};
+Profiler& profiler() {
+  static Profiler p;
+  return p;
+}
+constexpr size_t kMaxTimed = 4096;
+
+hipError_t launch_step_timed(const StepArgs& a, int D, hipStream_t s) {
+  Profiler& p = profiler();
+  std::pair<hipEvent_t, hipEvent_t>* slot = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(p.mu);
+    if (p.enabled && p.used < kMaxTimed) {
+      if (p.used == p.ev.size()) {
+        hipEvent_t e0, e1;
+        hipError_t e = hipEventCreate(&e0);
+        if (e != hipSuccess) return e;
+        e = hipEventCreate(&e1);
+        if (e != hipSuccess) return e;
+        p.ev.emplace_back(e0, e1);
+      }
+      slot = &p.ev[p.used++];
+    }
+  }
+  hipError_t e;
+  if (slot && (e = hipEventRecord(slot->first, s)) != hipSuccess) return e;
+  e = cpattn::launch_step(a, D, s);
+  if (e != hipSuccess) return e;
+  if (slot && (e = hipEventRecord(slot->second, s)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+// ---------------- ring-driver event pool (per device) ----------------
+std::mutex g_pool_mu;
+std::map<int, std::vector<hipEvent_t>> g_pools;
+
+cp_status_t get_events(int n, std::vector<hipEvent_t>& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  auto& pool = g_pools[dev];
+  while ((int)pool.size() < n) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    pool.push_back(ev);
+  }
+  out.assign(pool.begin(), pool.begin() + n);
+  return CP_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* cp_last_error(void) { return g_last_error.c_str(); }
+
+int cp_version(void) { return 100; }
+
+cp_status_t cp_zigzag_chunks(int cp_size, int rank, int chunk_len, int step, cp_chunks_t* q_chunks,
+                             cp_chunks_t* kv_chunks) {
+  if (cp_size < 1) return fail(CP_ERR_INVALID, "cp_size = %d must be >= 1", cp_size);
+  if (rank < 0 || rank >= cp_size) return fail(CP_ERR_INVALID, "rank = %d outside [0, %d)", rank, cp_size);
+  if (step < 0 || step >= cp_size) return fail(CP_ERR_INVALID, "step = %d outside [0, %d)", step, cp_size);
+  if (chunk_len <= 0) return fail(CP_ERR_INVALID, "chunk_len = %d must be > 0", chunk_len);
+  auto fill = [&](int r, cp_chunks_t* t) {
+    std::memset(t, 0, sizeof(*t));
+    t->n_chunks = 2;
+    t->chunk_len = chunk_len;
+    t->start[0] = (int64_t)r * chunk_len;                   // chunk r
+    t->start[1] = (int64_t)(2 * cp_size - 1 - r) * chunk_len;  // chunk 2N-1-r
+  };
+  if (q_chunks) fill(rank, q_chunks);
+  if (kv_chunks) fill(((rank - step) % cp_size + cp_size) % cp_size, kv_chunks);
+  g_last_error.clear();
+  return CP_OK;
+}
+
+cp_status_t cp_attn_step_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+                             void* out_bf16_or_null, int B, int H, int D, const cp_chunks_t* q_chunks,
+                             const cp_chunks_t* kv_chunks, float softmax_scale, int mode, hipStream_t stream) {
+  cp_status_t st = check_common(B, H, D, softmax_scale);
+  if (st != CP_OK) return st;
+  if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
+  if ((st = check_chunks(kv_chunks, "kv_chunks")) != CP_OK) return st;
+  if (mode != CP_STEP_WRITE && mode != CP_STEP_MERGE) return fail(CP_ERR_INVALID, "mode = %d unknown", mode);
+  if (!q || !k || !v || !o || !lse) return fail(CP_ERR_INVALID, "q, k, v, o and lse must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(out_bf16_or_null, 16))
+    return fail(CP_ERR_INVALID, "q, k, v, o, out must be 16-byte aligned and lse 4-byte aligned");
+  const size_t BH = (size_t)B * H;
+  const size_t Sq = (size_t)q_chunks->n_chunks * q_chunks->chunk_len;
+  const size_t Skv = (size_t)kv_chunks->n_chunks * kv_chunks->chunk_len;
+  const size_t qb = BH * Sq * D * 2, kvb = BH * Skv * D * 2, ob = BH * Sq * D * 4, lb = BH * Sq * 4;
+  const void* ins[3] = {q, k, v};
+  const size_t insz[3] = {qb, kvb, kvb};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(ins[i], insz[i], o, ob) || overlaps(ins[i], insz[i], lse, lb) ||
+        overlaps(ins[i], insz[i], out_bf16_or_null, qb))
+      return fail(CP_ERR_INVALID, "inputs must not alias o, lse or out");
+  if (overlaps(o, ob, lse, lb) || overlaps(o, ob, out_bf16_or_null, qb) || overlaps(lse, lb, out_bf16_or_null, qb))
+    return fail(CP_ERR_INVALID, "o, lse and out must not overlap");
+
+  StepArgs a;
+  base_args(a, q, k, v, o, lse, out_bf16_or_null, B, H, q_chunks, kv_chunks, softmax_scale);
+  std::vector<int> active;
+  std::vector<long long> work(CP_MAX_CHUNKS, 0);
+  for (int c = 0; c < q_chunks->n_chunks; ++c) {
+    work[c] = pairs_for_chunk(q_chunks, c, kv_chunks);
+    const bool needed = (mode == CP_STEP_WRITE) || work[c] > 0 || out_bf16_or_null != nullptr;
+    if (needed) active.push_back(c);
+    a.flags[c] = (mode == CP_STEP_MERGE ? cpattn::kFlagMerge : 0) | cpattn::kFlagWriteO |
+                 (out_bf16_or_null ? cpattn::kFlagFinalize : 0);
+  }
+  set_order(a, active, work);
+  hipError_t e = launch_step_timed(a, D, stream);
+  if (e != hipSuccess) return hip_fail(e, "step kernel launch");
+  g_last_error.clear();
+  return CP_OK;
+}
+
+cp_status_t cp_attn_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part, int B, int H,
+                          int Sq, int D, void* out_bf16_or_null, hipStream_t stream) {
+  if (B < 1 || H < 1 || Sq < 0) return fail(CP_ERR_INVALID, "B, H must be >= 1 and Sq >= 0");
+  if (D < 4 || D % 4 != 0) return fail(CP_ERR_INVALID, "D = %d must be a positive multiple of 4", D);
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return fail(CP_ERR_INVALID, "NULL operand");
+  if (!aligned(o_acc, 16) || !aligned(o_part, 16) || !aligned(out_bf16_or_null, 8) || !aligned(lse_acc, 4) ||
+      !aligned(lse_part, 4))
+    return fail(CP_ERR_INVALID, "o_acc/o_part must be 16-byte, out 8-byte, lse 4-byte aligned");
+  const int64_t rows = (int64_t)B * H * Sq;
+  const size_t ob = (size_t)rows * D * 4, lb = (size_t)rows * 4;
+  if (overlaps(o_acc, ob, o_part, ob) || overlaps(lse_acc, lb, lse_part, lb) || overlaps(o_acc, ob, lse_acc, lb) ||
+      overlaps(o_acc, ob, lse_part, lb) || overlaps(lse_acc, lb, o_part, ob) ||
+      overlaps(out_bf16_or_null, (size_t)rows * D * 2, o_acc, ob) ||
+      overlaps(out_bf16_or_null, (size_t)rows * D * 2, o_part, ob))
+    return fail(CP_ERR_INVALID, "merge operands must not overlap");
+  hipError_t e = cpattn::launch_merge(o_acc, lse_acc, o_part, lse_part, static_cast<uint16_t*>(out_bf16_or_null),
+                                      rows, D, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  g_last_error.clear();
+  return CP_OK;
+}
+
+size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq) {
+  if (B <= 0 || H <= 0 || Skv <= 0 || D <= 0 || Sq <= 0) return 0;
+  const size_t kv = round256((size_t)B * H * Skv * D * 2);
+  const size_t o = round256((size_t)B * H * Sq * D * 4);
+  return 4 * kv + o;
+}
+
+cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const void* const* k_steps,
+                             const void* const* v_steps, const cp_chunks_t* kv_chunks_steps, int n_steps, void* out,
+                             float* lse, int B, int H, int D, float softmax_scale, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, hipStream_t copy_stream) {
+  cp_status_t st = check_common(B, H, D, softmax_scale);
+  if (st != CP_OK) return st;
+  if (n_steps < 1 || n_steps > CP_MAX_STEPS)
+    return fail(CP_ERR_INVALID, "n_steps = %d outside [1, %d]", n_steps, CP_MAX_STEPS);
+  if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
+  if (!k_steps || !v_steps || !kv_chunks_steps) return fail(CP_ERR_INVALID, "k_steps, v_steps, kv_chunks_steps NULL");
+  for (int j = 0; j < n_steps; ++j) {
+    char name[48];
+    snprintf(name, sizeof(name), "kv_chunks_steps[%d]", j);
+    if ((st = check_chunks(&kv_chunks_steps[j], name)) != CP_OK) return st;
+    if (kv_chunks_steps[j].n_chunks != kv_chunks_steps[0].n_chunks ||
+        kv_chunks_steps[j].chunk_len != kv_chunks_steps[0].chunk_len)
+      return fail(CP_ERR_INVALID, "every step's K/V table must have the same n_chunks and chunk_len");
+    if (!k_steps[j] || !v_steps[j] || !aligned(k_steps[j], 16) || !aligned(v_steps[j], 16))
+      return fail(CP_ERR_INVALID, "k_steps[%d] / v_steps[%d] NULL or not 16-byte aligned", j, j);
+  }
+  if (!q || !out || !lse) return fail(CP_ERR_INVALID, "q, out and lse must be non-NULL");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return fail(CP_ERR_INVALID, "q, out must be 16-byte aligned and lse 4-byte aligned");
+  if (!workspace || !aligned(workspace, 256)) return fail(CP_ERR_INVALID, "workspace NULL or not 256-byte aligned");
+  if (!copy_stream || copy_stream == stream)
+    return fail(CP_ERR_INVALID, "copy_stream must be a stream other than stream");
+  const int Sq = q_chunks->n_chunks * q_chunks->chunk_len;
+  const int Skv = kv_chunks_steps[0].n_chunks * kv_chunks_steps[0].chunk_len;
+  const size_t need = cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq);
+  if (workspace_bytes < need)
+    return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t BH = (size_t)B * H;
+  const size_t kv_bytes = BH * Skv * D * 2, q_bytes = BH * Sq * D * 2, lse_bytes = BH * Sq * 4;
+  // no operand may overlap the workspace or the outputs
+  const void* outs[3] = {workspace, out, lse};
+  const size_t outsz[3] = {need, q_bytes, lse_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(q, q_bytes, outs[i], outsz[i])) return fail(CP_ERR_INVALID, "q overlaps an output or the workspace");
+    for (int j = 0; j < n_steps; ++j)
+      if (overlaps(k_steps[j], kv_bytes, outs[i], outsz[i]) || overlaps(v_steps[j], kv_bytes, outs[i], outsz[i]))
+        return fail(CP_ERR_INVALID, "K/V of step %d overlaps an output or the workspace", j);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j]))
+        return fail(CP_ERR_INVALID, "out, lse and workspace must not overlap");
+  }
+
+  // ---- plan: which query chunks work at which step, and how ----
+  const int nq = q_chunks->n_chunks;
+  std::vector<std::vector<long long>> work(n_steps, std::vector<long long>(CP_MAX_CHUNKS, 0));
+  std::vector<int> first(nq, -1), last(nq, -1);
+  for (int j = 0; j < n_steps; ++j)
+    for (int c = 0; c < nq; ++c) {
+      work[j][c] = pairs_for_chunk(q_chunks, c, &kv_chunks_steps[j]);
+      if (work[j][c] > 0) {
+        if (first[c] < 0) first[c] = j;
+        last[c] = j;
+      }
+    }
+  for (int c = 0; c < nq; ++c)
+    if (first[c] < 0) first[c] = last[c] = n_steps - 1;  // no key at all: write O = 0, LSE = -inf
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const size_t kv_slot = round256(kv_bytes);
+  void* slot_k[2] = {ws, ws + 2 * kv_slot};
+  void* slot_v[2] = {ws + kv_slot, ws + 3 * kv_slot};
+  float* o_run = reinterpret_cast<float*>(ws + 4 * kv_slot);
+
+  std::vector<hipEvent_t> ev;
+  if ((st = get_events(2 + 2 * n_steps, ev)) != CP_OK) return st;
+  hipEvent_t ev_entry = ev[0], ev_done = ev[1];
+  hipEvent_t* copied = &ev[2];
+  hipEvent_t* released = &ev[2 + n_steps];
+
+  hipError_t e;
+#define HIP_TRY(call, what)                 \
+  do {                                      \
+    if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
+  } while (0)
+
+  auto stage = [&](int j) -> cp_status_t {  // copy step j's block into slot j%2 on copy_stream
+    if (j >= 3) HIP_TRY(hipStreamWaitEvent(copy_stream, released[j - 2], 0), "hipStreamWaitEvent");
+    HIP_TRY(hipMemcpyAsync(slot_k[j & 1], k_steps[j], kv_bytes, hipMemcpyDeviceToDevice, copy_stream),
+            "hipMemcpyAsync(K)");
+    HIP_TRY(hipMemcpyAsync(slot_v[j & 1], v_steps[j], kv_bytes, hipMemcpyDeviceToDevice, copy_stream),
+            "hipMemcpyAsync(V)");
+    HIP_TRY(hipEventRecord(copied[j], copy_stream), "hipEventRecord");
+    return CP_OK;
+  };
+
+  HIP_TRY(hipEventRecord(ev_entry, stream), "hipEventRecord");
+  HIP_TRY(hipStreamWaitEvent(copy_stream, ev_entry, 0), "hipStreamWaitEvent");
+  if (n_steps > 1 && (st = stage(1)) != CP_OK) return st;
+  for (int j = 0; j < n_steps; ++j) {
+    // the copy for step j+1 goes into the slot step j-1 read; it overlaps step j
+    if (j + 1 >= 2 && j + 1 < n_steps && (st = stage(j + 1)) != CP_OK) return st;
+    if (j >= 1) HIP_TRY(hipStreamWaitEvent(stream, copied[j], 0), "hipStreamWaitEvent");
+    const void* kj = (j == 0) ? k_steps[0] : slot_k[j & 1];
+    const void* vj = (j == 0) ? v_steps[0] : slot_v[j & 1];
+    StepArgs a;
+    base_args(a, q, kj, vj, o_run, lse, out, B, H, q_chunks, &kv_chunks_steps[j], softmax_scale);
+    std::vector<int> active;
+    for (int c = 0; c < nq; ++c) {
+      if (j < first[c] || j > last[c] || (work[j][c] == 0 && j != last[c] && j != first[c])) continue;
+      active.push_back(c);
+      a.flags[c] = (j == first[c] ? 0 : cpattn::kFlagMerge) |
+                   (j == last[c] ? cpattn::kFlagFinalize : cpattn::kFlagWriteO);
+    }
+    set_order(a, active, work[j]);
+    HIP_TRY(launch_step_timed(a, D, stream), "step kernel launch");
+    if (j + 2 < n_steps) HIP_TRY(hipEventRecord(released[j], stream), "hipEventRecord");
+  }
+  HIP_TRY(hipEventRecord(ev_done, copy_stream), "hipEventRecord");
+  HIP_TRY(hipStreamWaitEvent(stream, ev_done, 0), "hipStreamWaitEvent");
+#undef HIP_TRY
+  g_last_error.clear();
+  return CP_OK;
+}
+
+cp_status_t cp_profile_enable(int enable) {
+  Profiler& p = profiler();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.enabled = enable != 0;
+  p.used = 0;
+  return CP_OK;
+}
+
+cp_status_t cp_profile_read(float* kernel_ms, int max_entries, int* n_entries) {
+  Profiler& p = profiler();
+  std::lock_guard<std::mutex> lk(p.mu);
+  int n = 0;
+  for (size_t i = 0; i < p.used; ++i) {
+    hipError_t e = hipEventSynchronize(p.ev[i].second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    if (kernel_ms && n < max_entries) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, p.ev[i].first, p.ev[i].second);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      kernel_ms[n] = ms;
+    }
+    if (n < max_entries) ++n;
+  }
+  if (n_entries) *n_entries = n;
+  p.used = 0;
+  g_last_error.clear();
+  return CP_OK;
+}
+
+}  // extern "C"

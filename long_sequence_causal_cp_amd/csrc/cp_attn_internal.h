@@ -1,0 +1,52 @@
+// Internal interface between the host library (validation, ring driver) and
+// the gfx950 kernels.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+constexpr int kMaxChunks = 8;
+constexpr int kTileKeys = 64;  // keys per K/V tile staged through LDS
+
+// Per-query-chunk work flags for one step launch.
+enum : int {
+  kFlagMerge = 1,     // read the running (O, LSE) and merge; else overwrite
+  kFlagFinalize = 2,  // write bf16 output
+  kFlagWriteO = 4,    // write the fp32 running O
+};
+
+// Everything one launch of the step kernel needs; passed by value.
+struct StepArgs {
+  const uint16_t* q;  // bf16 [BH, Sq, D]
+  const uint16_t* k;  // bf16 [BH, Skv, D]
+  const uint16_t* v;  // bf16 [BH, Skv, D]
+  float* o_run;       // fp32 [BH, Sq, D] (may be null when no chunk has kFlagWriteO/kFlagMerge)
+  float* lse_run;     // fp32 [BH, Sq]
+  uint16_t* out;      // bf16 [BH, Sq, D] (may be null when no chunk finalizes)
+  int BH;
+  int Sq, Skv;
+  int q_chunk_len, kv_chunk_len;
+  int n_kv_chunks;
+  int n_order;                // active query chunks in this launch
+  int order[kMaxChunks];      // their indices, heaviest first
+  int flags[kMaxChunks];      // per query chunk index
+  int q_start[kMaxChunks];    // absolute positions
+  int kv_start[kMaxChunks];
+  int rb_per_chunk;           // row blocks per query chunk
+  int heads_per_xcd;          // > 0: keep each (b,h) on one XCD
+  float scale_log2;           // tau * log2(e)
+};
+
+// Row-block height (queries per workgroup) the step kernel uses for a chunk length.
+int step_block_rows(int q_chunk_len);
+
+// Launch the step kernel; `grid` = n_order * rb_per_chunk * BH workgroups.
+hipError_t launch_step(const StepArgs& a, int D, hipStream_t stream);
+
+// Standalone merge kernel.
+hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                        uint16_t* out, int64_t rows, int D, hipStream_t stream);
+
+}  // namespace cpattn

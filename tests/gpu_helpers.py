@@ -1,0 +1,96 @@
+"""Shared plumbing for the GPU parity tests: rank buffers, ring calls, oracle rows.
+
+Rank buffers are gathered from the full sequence with the library's own
+chunk tables (cp_zigzag_chunks); expected values come from the fp64 oracle
+with its own index maths.  The oracle runs per (batch, head) in a thread
+pool (numpy releases the GIL in matmul and exp), at most 16 threads.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+import oracle
+import long_sequence_causal_cp_amd as cp
+
+OUT_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+def threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def positions(table):
+    return np.concatenate([np.arange(s, s + table.chunk_len) for s in table.starts()])
+
+
+def gather(x, table, dev):
+    idx = torch.from_numpy(positions(table))
+    return x.index_select(2, idx).contiguous().to(dev)
+
+
+def zigzag_tables(cp_size, rank, L):
+    q_tab = cp.cp_zigzag_chunks(cp_size, rank, L, 0)[0]
+    kv = [cp.cp_zigzag_chunks(cp_size, rank, L, j)[1] for j in range(cp_size)]
+    return q_tab, kv
+
+
+def run_ring(Q, K, V, q_tab, kv_tabs, scale, dev, stream=None, copy_stream=None, kv_cache=None):
+    """Gather the rank's Q and each step's K/V, run cp_ring_attn_fwd; returns (out, lse) on device."""
+    B, H, _, D = Q.shape
+    q = gather(Q, q_tab, dev)
+    ks, vs = [], []
+    for t in kv_tabs:
+        key = tuple(t.starts())
+        if kv_cache is not None and key in kv_cache:
+            kk, vv = kv_cache[key]
+        else:
+            kk, vv = gather(K, t, dev), gather(V, t, dev)
+            if kv_cache is not None:
+                kv_cache[key] = (kk, vv)
+        ks.append(kk)
+        vs.append(vv)
+    Sq, Skv = q.shape[2], ks[0].shape[2]
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    ws = torch.empty(cp.cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq), dtype=torch.uint8, device=dev)
+    copy_stream = copy_stream or torch.cuda.Stream()
+    cp.cp_ring_attn_fwd(q, q_tab, ks, vs, kv_tabs, out, lse, scale, ws, stream=stream, copy_stream=copy_stream)
+    return out, lse
+
+
+def oracle_rows(Q, K, V, pos_per_head, scale):
+    """Oracle (out, lse) at absolute positions pos_per_head [B, H, n] (bf16 inputs, fp64 maths)."""
+    B, H = Q.shape[:2]
+    n = pos_per_head.shape[-1]
+    D = V.shape[-1]
+    out = np.empty((B, H, n, D))
+    lse = np.empty((B, H, n))
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        rows = pos_per_head[b, h]
+        kmax = int(rows.max()) + 1
+        q = oracle.to_f64(Q[b, h])
+        k = oracle.to_f64(K[b, h, :kmax])
+        v = oracle.to_f64(V[b, h, :kmax])
+        out[b, h], lse[b, h] = oracle.causal_attention_rows(q, k, v, rows, scale)
+
+    with ThreadPoolExecutor(threads()) as ex:
+        list(ex.map(one, range(B * H)))
+    return out, lse
+
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, local_rows=None):
+    """Max-abs errors of GPU results (optionally at local_rows [B,H,n]) against the oracle's."""
+    o = out_gpu.float().cpu().numpy()
+    l = lse_gpu.cpu().numpy()
+    if local_rows is not None:
+        o = np.take_along_axis(o, local_rows[..., None], axis=2)
+        l = np.take_along_axis(l, local_rows, axis=2)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    return float(np.max(np.abs(o - out_ref))), float(np.max(np.abs(l - lse_ref)))

@@ -1,0 +1,163 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library must load, export every function include/cp_attn.h declares, and
+reject bad arguments with the documented status before touching the GPU.
+Only argument paths that fail validation are called here; device pointers are
+fake (never dereferenced).
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from long_sequence_causal_cp_amd import binding as cb
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+ALIGNED = 0x7F0000000000        # fake, 256-byte aligned device addresses
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cb.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return cb.load_library()
+
+
+def fake(i):
+    return ctypes.c_void_p(ALIGNED + i * 1024 * MB)
+
+
+def test_every_header_function_is_exported(lib):
+    names = cb.header_functions()
+    assert "cp_ring_attn_fwd" in names and "cp_attn_step_fwd" in names and "cp_attn_merge" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", cb.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_version(lib):
+    assert cb.cp_version() >= 100
+
+
+def test_zigzag_matches_pages_worked_example(lib):
+    with open(os.path.join(GOLDEN, "zigzag_cp4.txt")) as f:
+        rows = [tuple(map(int, l.split())) for l in f if l.strip() and not l.startswith("#")]
+    for r, a, b in rows:
+        q, kv = cb.cp_zigzag_chunks(4, r, 10, 0)
+        assert q.n_chunks == 2 and q.chunk_len == 10
+        assert q.starts() == [10 * a, 10 * b]
+        assert kv.starts() == q.starts()
+
+
+@pytest.mark.parametrize("cp", [1, 2, 4, 8, 16])
+def test_zigzag_ring_matches_oracle_index_maths(lib, cp):
+    L = 64
+    S = 2 * cp * L
+    for r in range(cp):
+        for j in range(cp):
+            q, kv = cb.cp_zigzag_chunks(cp, r, L, j)
+            qpos = [s + i for s in q.starts() for i in range(L)]
+            kpos = [s + i for s in kv.starts() for i in range(L)]
+            assert qpos == list(oracle.local_positions(S, cp, r))
+            assert kpos == list(oracle.ring_kv_positions(S, cp, r, j))
+
+
+@pytest.mark.parametrize("args", [(0, 0, 64, 0), (2, 2, 64, 0), (2, -1, 64, 0), (2, 0, 64, 2), (2, 0, 0, 0)])
+def test_zigzag_rejects_bad_arguments(lib, args):
+    with pytest.raises(cb.CpError) as e:
+        cb.cp_zigzag_chunks(*args)
+    assert e.value.status == cb.CP_ERR_INVALID
+    assert cb.cp_last_error()
+
+
+def test_workspace_bytes(lib):
+    B, H, Skv, D, Sq = 1, 32, 4096, 128, 4096
+    kv = B * H * Skv * D * 2
+    assert cb.cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq) == 4 * kv + B * H * Sq * D * 4
+    assert cb.cp_ring_attn_workspace_bytes(1, 1, 64, 64, 64) % 256 == 0
+    assert cb.cp_ring_attn_workspace_bytes(0, 1, 64, 64, 64) == 0
+
+
+def _step(lib, D=128, qt=None, kvt=None, scale=0.088, mode=0, q=None, o=None, lse=None, out=None, B=1, H=2):
+    qt = qt or cb.CpChunks.make([0, 192], 64)
+    kvt = kvt or cb.CpChunks.make([0, 192], 64)
+    return lib.cp_attn_step_fwd(q or fake(0), fake(1), fake(2), o or fake(3), lse or fake(4), out,
+                                B, H, D, ctypes.byref(qt), ctypes.byref(kvt), scale, mode, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), cb.CP_ERR_UNSUPPORTED),
+    (dict(D=32), cb.CP_ERR_UNSUPPORTED),
+    (dict(B=0), cb.CP_ERR_INVALID),
+    (dict(scale=float("nan")), cb.CP_ERR_INVALID),
+    (dict(scale=0.0), cb.CP_ERR_INVALID),
+    (dict(scale=float("inf")), cb.CP_ERR_INVALID),
+    (dict(mode=7), cb.CP_ERR_INVALID),
+    (dict(qt=cb.CpChunks.make([0, 192], 48)), cb.CP_ERR_INVALID),        # chunk_len not multiple of 64
+    (dict(qt=cb.CpChunks.make([0, 32], 64)), cb.CP_ERR_INVALID),         # overlapping chunks
+    (dict(kvt=cb.CpChunks.make([-64], 64)), cb.CP_ERR_INVALID),          # negative start
+    (dict(kvt=cb.CpChunks.make([2**31 - 64], 128)), cb.CP_ERR_INVALID),  # positions overflow int32
+    (dict(qt=cb.CpChunks.make([], 64)), cb.CP_ERR_INVALID),              # no chunks
+    (dict(q=ctypes.c_void_p(ALIGNED + 8)), cb.CP_ERR_INVALID),           # misaligned
+    (dict(o=fake(0)), cb.CP_ERR_INVALID),                                # o aliases q
+    (dict(out=fake(3)), cb.CP_ERR_INVALID),                              # out aliases o
+])
+def test_step_fwd_validation(lib, kw, status):
+    assert _step(lib, **kw) == status
+    assert cb.cp_last_error()
+
+
+def test_step_fwd_too_many_chunks(lib):
+    t = cb.CpChunks()
+    t.n_chunks = 9
+    t.chunk_len = 64
+    assert lib.cp_attn_step_fwd(fake(0), fake(1), fake(2), fake(3), fake(4), None, 1, 1, 128,
+                                ctypes.byref(t), ctypes.byref(t), 0.1, 0, None) == cb.CP_ERR_INVALID
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=6), cb.CP_ERR_INVALID),
+    (dict(B=0), cb.CP_ERR_INVALID),
+    (dict(o_part=fake(0)), cb.CP_ERR_INVALID),
+    (dict(o_acc=ctypes.c_void_p(ALIGNED + 4)), cb.CP_ERR_INVALID),
+])
+def test_merge_validation(lib, kw, status):
+    a = dict(o_acc=fake(0), lse_acc=fake(1), o_part=fake(2), lse_part=fake(3), B=1, H=1, Sq=64, D=128)
+    a.update(kw)
+    assert lib.cp_attn_merge(a["o_acc"], a["lse_acc"], a["o_part"], a["lse_part"], a["B"], a["H"],
+                             a["Sq"], a["D"], None, None) == status
+
+
+def _ring(lib, n_steps=2, ws_bytes=None, copy_stream=ctypes.c_void_p(0x1234), kv_override=None,
+          workspace=None, stream=None, out=None):
+    L = 64
+    qt = cb.CpChunks.make([0, 192], L)
+    tabs = [cb.cp_zigzag_chunks(2, 0, L, j % 2)[1] for j in range(max(n_steps, 1))]
+    if kv_override is not None:
+        tabs[1] = kv_override
+    T = cb.CpChunks * len(tabs)
+    ks = (ctypes.c_void_p * len(tabs))(*[ALIGNED + (10 + j) * 1024 * MB for j in range(len(tabs))])
+    vs = (ctypes.c_void_p * len(tabs))(*[ALIGNED + (40 + j) * 1024 * MB for j in range(len(tabs))])
+    need = cb.cp_ring_attn_workspace_bytes(1, 2, 128, 128, 128)
+    return lib.cp_ring_attn_fwd(fake(0), ctypes.byref(qt), ks, vs, T(*tabs), n_steps, out or fake(1), fake(2),
+                                1, 2, 128, 0.088, workspace or fake(3), need if ws_bytes is None else ws_bytes,
+                                stream, copy_stream)
+
+
+def test_ring_validation(lib):
+    assert _ring(lib, n_steps=0) == cb.CP_ERR_INVALID
+    assert _ring(lib, n_steps=65) == cb.CP_ERR_INVALID
+    assert _ring(lib, ws_bytes=1000) == cb.CP_ERR_WORKSPACE
+    assert "needed" in cb.cp_last_error()
+    assert _ring(lib, copy_stream=None) == cb.CP_ERR_INVALID
+    assert _ring(lib, copy_stream=ctypes.c_void_p(0x99), stream=ctypes.c_void_p(0x99)) == cb.CP_ERR_INVALID
+    assert _ring(lib, kv_override=cb.CpChunks.make([0, 128, 192], 64)) == cb.CP_ERR_INVALID
+    assert _ring(lib, workspace=ctypes.c_void_p(ALIGNED + 128)) == cb.CP_ERR_INVALID   # misaligned
+    assert _ring(lib, workspace=fake(1)) == cb.CP_ERR_INVALID                           # overlaps out
+    assert _ring(lib, out=fake(10)) == cb.CP_ERR_INVALID                                # out overlaps K

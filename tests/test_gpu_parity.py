@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path against the fp64 oracle, through the C ABI.
+
+Tolerances (max-abs over every compared element): bf16 output 2e-2, natural
+LSE 1e-3, fp32 partial O 2e-2.  Inputs are the seeded bf16 workloads; the
+oracle consumes the same bf16 values.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import long_sequence_causal_cp_amd as cp
+from gpu_helpers import (LSE_TOL, OUT_TOL, compare, gather, oracle_rows, positions, run_ring,
+                         zigzag_tables)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    cp.load_library()
+
+
+def _announce(*a):
+    print("[case]", *a, flush=True)
+
+
+# ---------------------------------------------------------------- step level
+@pytest.mark.parametrize("name", ["tiny", "s8k_cp2"])
+def test_step_partials_and_merge_chain(name):
+    w = workloads.get(name)
+    Q, K, V = workloads.make_qkv(w)
+    L, N = w.chunk_len, w.cp
+    for r in range(N):
+        _announce(name, "rank", r)
+        q_tab, kv_tabs = zigzag_tables(N, r, L)
+        qpos = positions(q_tab)
+        q = gather(Q, q_tab, DEV)
+        Sq = q.shape[2]
+        o_run = torch.empty((w.B, w.H, Sq, w.D), dtype=torch.float32, device=DEV)
+        lse_run = torch.empty((w.B, w.H, Sq), dtype=torch.float32, device=DEV)
+        for j, t in enumerate(kv_tabs):
+            k, v = gather(K, t, DEV), gather(V, t, DEV)
+            # partial of this block alone
+            o = torch.empty_like(o_run)
+            lse = torch.empty_like(lse_run)
+            out = torch.empty_like(q)
+            cp.cp_attn_step_fwd(q, k, v, o, lse, out, q_tab, t, w.scale, cp.CP_STEP_WRITE)
+            # running merge chain
+            cp.cp_attn_step_fwd(q, k, v, o_run, lse_run, None, q_tab, t, w.scale,
+                                cp.CP_STEP_WRITE if j == 0 else cp.CP_STEP_MERGE)
+            torch.cuda.synchronize()
+            kpos = positions(t)
+            qf, kf, vf = (oracle.to_f64(x) for x in (q.cpu(), k.cpu(), v.cpu()))
+            ro = np.empty((w.B, w.H, Sq, w.D))
+            rl = np.empty((w.B, w.H, Sq))
+            for b in range(w.B):
+                for h in range(w.H):
+                    ro[b, h], rl[b, h] = oracle.masked_attention(qf[b, h], qpos, kf[b, h], vf[b, h], kpos, w.scale)
+            og, lg, outg = o.cpu().numpy(), lse.cpu().numpy(), out.float().cpu().numpy()
+            empty = np.isneginf(rl)
+            assert np.array_equal(np.isneginf(lg), empty)
+            assert np.all(og[empty] == 0) and np.all(outg[empty] == 0)
+            full = ~empty
+            if full.any():
+                assert np.max(np.abs(og[full] - ro[full])) <= OUT_TOL
+                assert np.max(np.abs(outg[full] - ro[full])) <= OUT_TOL
+                assert np.max(np.abs(lg[full] - rl[full])) <= LSE_TOL
+        ro, rl = oracle_rows(Q, K, V, np.broadcast_to(qpos, (w.B, w.H, Sq)), w.scale)
+        eo = np.max(np.abs(o_run.cpu().numpy() - ro))
+        el = np.max(np.abs(lse_run.cpu().numpy() - rl))
+        assert eo <= OUT_TOL and el <= LSE_TOL, (eo, el)
+
+
+@pytest.mark.parametrize("D,Sq", [(128, 4096), (64, 333), (12, 50), (1028, 7)])
+def test_merge_kernel(D, Sq):
+    _announce("merge", D, Sq)
+    g = torch.Generator().manual_seed(D * 1000 + Sq)
+    B, H = 2, 3
+    oa = torch.randn(B, H, Sq, D, generator=g)
+    ob = torch.randn(B, H, Sq, D, generator=g)
+    la = torch.randn(B, H, Sq, generator=g) * 4
+    lb = torch.randn(B, H, Sq, generator=g) * 4
+    la[0, 0, ::3] = -math.inf
+    lb[0, 0, ::5] = -math.inf
+    lb[1, 2, ::2] = -math.inf
+    oa[la == -math.inf] = 0
+    ob[lb == -math.inf] = 0
+    ro, rl = oracle.lse_merge(oa.double().numpy(), la.double().numpy(), ob.double().numpy(), lb.double().numpy())
+    o_acc, l_acc = oa.to(DEV), la.to(DEV)
+    out = torch.empty(B, H, Sq, D, dtype=torch.bfloat16, device=DEV)
+    cp.cp_attn_merge(o_acc, l_acc, ob.to(DEV), lb.to(DEV), out)
+    torch.cuda.synchronize()
+    lg = l_acc.cpu().numpy()
+    assert np.array_equal(np.isneginf(lg), np.isneginf(rl))
+    fin = ~np.isneginf(rl)
+    assert np.max(np.abs(lg[fin] - rl[fin])) <= 1e-5
+    assert np.max(np.abs(o_acc.cpu().numpy() - ro)) <= 1e-5
+    assert np.max(np.abs(out.float().cpu().numpy() - ro)) <= 2e-2
+
+
+# ---------------------------------------------------------------- full ring
+RING_CASES = [
+    ("tiny", r, None) for r in range(2)
+] + [
+    ("s8k_cp2", r, None) for r in range(2)
+] + [
+    ("s16k_cp4", r, 256) for r in range(4)
+] + [
+    ("s32k_cp8", 0, 128), ("s32k_cp8", 7, 128),
+    ("s64k_cp16", 0, 512),
+]
+
+_QKV = {}
+
+
+def _qkv(name):
+    if name not in _QKV:
+        _QKV.clear()
+        _QKV[name] = workloads.make_qkv(workloads.get(name))
+    return _QKV[name]
+
+
+@pytest.mark.parametrize("name,rank,rows", RING_CASES)
+def test_ring_parity(name, rank, rows):
+    w = workloads.get(name)
+    _announce("ring", w.describe(), "rank", rank, "rows/head", rows or "all")
+    Q, K, V = _qkv(name)
+    q_tab, kv_tabs = zigzag_tables(w.cp, rank, w.chunk_len)
+    out, lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV)
+    torch.cuda.synchronize()
+    qpos = positions(q_tab)
+    if rows is None:
+        local = np.broadcast_to(np.arange(len(qpos)), (w.B, w.H, len(qpos))).copy()
+    else:
+        local = workloads.sample_local_rows(w, n_rows=rows)
+    ro, rl = oracle_rows(Q, K, V, qpos[local], w.scale)
+    eo, el = compare(out, lse, ro, rl, local)
+    print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
+    assert eo <= OUT_TOL and el <= LSE_TOL, (eo, el)
+
+
+# ---------------------------------------------------------------- invariants
+def _small(name="s8k_cp2", H=4, S=None):
+    w = workloads.get(name)
+    return w, (w.B, H, S or w.S, w.D)
+
+
+def test_ring_q_zero_closed_form():
+    w, shape = _small(H=2)
+    _, K, V = workloads.make_qkv(w, H=2)
+    Q = torch.zeros(shape, dtype=torch.bfloat16)
+    for r in range(w.cp):
+        q_tab, kv_tabs = zigzag_tables(w.cp, r, w.chunk_len)
+        out, lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV)
+        torch.cuda.synchronize()
+        pos = positions(q_tab)
+        lg = lse.cpu().numpy()
+        assert np.max(np.abs(lg - np.log(pos + 1.0))) <= LSE_TOL
+        mean = np.cumsum(oracle.to_f64(V), axis=2) / np.arange(1, w.S + 1)[:, None]
+        assert np.max(np.abs(out.float().cpu().numpy() - mean[:, :, pos])) <= OUT_TOL
+
+
+def test_ring_constant_v_and_first_token():
+    w, shape = _small(H=2)
+    Q, K, _ = workloads.make_qkv_scaled(shape, 77, q_scale=3.0, k_scale=3.0)
+    c = torch.linspace(-2, 2, w.D).to(torch.bfloat16)
+    V = c.expand(shape).contiguous()
+    q_tab, kv_tabs = zigzag_tables(w.cp, 0, w.chunk_len)
+    out, lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(out.float().cpu().numpy() - c.float().numpy())) <= 1e-2
+    # position 0 is local row 0 of rank 0: it sees only itself
+    q0, k0 = oracle.to_f64(Q[:, :, 0]), oracle.to_f64(K[:, :, 0])
+    assert np.max(np.abs(lse[:, :, 0].cpu().numpy() - (q0 * k0).sum(-1) * w.scale)) <= LSE_TOL
+
+
+@pytest.mark.parametrize("qs,ks", [(1.0, 1.0), (3.0, 3.0), (0.2, 6.0)])
+def test_ring_peaked_and_flat_softmax(qs, ks):
+    w, shape = _small(H=4)
+    Q, K, V = workloads.make_qkv_scaled(shape, 11, q_scale=qs, k_scale=ks)
+    for r in range(w.cp):
+        q_tab, kv_tabs = zigzag_tables(w.cp, r, w.chunk_len)
+        out, lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV)
+        torch.cuda.synchronize()
+        pos = positions(q_tab)
+        ro, rl = oracle_rows(Q, K, V, np.broadcast_to(pos, (w.B, 4, len(pos))), w.scale)
+        eo, el = compare(out, lse, ro, rl)
+        assert eo <= OUT_TOL and el <= LSE_TOL, (qs, ks, r, eo, el)
+
+
+def test_ring_needle_keys():
+    """Keys equal to 4x a later query make single keys dominate their rows."""
+    w, shape = _small(H=2)
+    Q, K, V = workloads.make_qkv_scaled(shape, 5)
+    rng = np.random.default_rng(0)
+    for i in rng.choice(w.S - 1, size=64, replace=False):
+        j = int(rng.integers(i + 1, w.S))
+        K[:, :, i] = (Q[:, :, j].float() * 4).to(torch.bfloat16)
+    q_tab, kv_tabs = zigzag_tables(w.cp, 1, w.chunk_len)
+    out, lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV)
+    torch.cuda.synchronize()
+    pos = positions(q_tab)
+    ro, rl = oracle_rows(Q, K, V, np.broadcast_to(pos, (w.B, 2, len(pos))), w.scale)
+    eo, el = compare(out, lse, ro, rl)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+
+
+def test_contiguous_and_permuted_tables():
+    """The ABI takes any chunk tables: contiguous sharding and a permuted ring order."""
+    name = "s16k_cp4"
+    w = workloads.get(name)
+    H = 2
+    Q, K, V = workloads.make_qkv(w, H=H)
+    N = w.cp
+    n = w.S // N
+    # contiguous: rank r holds [r n, (r+1) n) as one chunk; step j gets rank (r-j) mod N
+    for r in (0, N - 1):
+        q_tab = cp.CpChunks.make([r * n], n)
+        kv_tabs = [cp.CpChunks.make([((r - j) % N) * n], n) for j in range(N)]
+        out, lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV)
+        torch.cuda.synchronize()
+        pos = positions(q_tab)
+        local = np.stack([np.sort(np.random.default_rng(r).choice(n, 256, replace=False))] * H)[None]
+        ro, rl = oracle_rows(Q, K, V, pos[local], w.scale)
+        eo, el = compare(out, lse, ro, rl, local)
+        assert eo <= OUT_TOL and el <= LSE_TOL, ("contiguous", r, eo, el)
+    # zigzag with the steps after the first in reverse order: same result
+    q_tab, kv_tabs = zigzag_tables(N, 2, w.chunk_len)
+    out1, lse1 = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV)
+    out2, lse2 = run_ring(Q, K, V, q_tab, [kv_tabs[0]] + kv_tabs[1:][::-1], w.scale, DEV)
+    torch.cuda.synchronize()
+    assert (out1.float() - out2.float()).abs().max().item() <= 2e-2
+    assert (lse1 - lse2).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("D,L", [(128, 64), (64, 128), (64, 64), (128, 192)])
+def test_kernel_variants(D, L):
+    """All four compiled step-kernel variants (D in {64,128}, 64- and 128-row blocks)."""
+    _announce("variant", D, L)
+    N, H = 3, 2
+    S = 2 * N * L
+    Q, K, V = workloads.make_qkv_scaled((1, H, S, D), D + L)
+    for r in range(N):
+        q_tab, kv_tabs = zigzag_tables(N, r, L)
+        out, lse = run_ring(Q, K, V, q_tab, kv_tabs, 1 / math.sqrt(D), DEV)
+        torch.cuda.synchronize()
+        pos = positions(q_tab)
+        ro, rl = oracle_rows(Q, K, V, np.broadcast_to(pos, (1, H, len(pos))), 1 / math.sqrt(D))
+        eo, el = compare(out, lse, ro, rl)
+        assert eo <= OUT_TOL and el <= LSE_TOL, (r, eo, el)
+
+
+def test_full_sequence_single_step():
+    """All-gather variant: the whole sequence as one query block against all keys in one step."""
+    w = workloads.get("s8k_cp2")
+    H = 2
+    Q, K, V = workloads.make_qkv(w, H=H)
+    t = cp.CpChunks.make([0], w.S)
+    q, k, v = (x.contiguous().to(DEV) for x in (Q, K, V))
+    o = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+    out = torch.empty_like(q)
+    cp.cp_attn_step_fwd(q, k, v, o, lse, out, t, t, w.scale, cp.CP_STEP_WRITE)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(3).choice(w.S, 512, replace=False))
+    ro, rl = oracle_rows(Q, K, V, np.broadcast_to(rows, (1, H, 512)), w.scale)
+    eo, el = compare(out, lse, ro, rl, np.broadcast_to(rows, (1, H, 512)).copy())
+    assert eo <= OUT_TOL and el <= LSE_TOL
+
+
+# ---------------------------------------------------------------- stream ordering
+def test_ring_unchanged_by_stream_delays():
+    """Delays injected on either stream must not change a single bit of the result."""
+    w = workloads.get("s16k_cp4")
+    H = 4
+    Q, K, V = workloads.make_qkv(w, H=H)
+    q_tab, kv_tabs = zigzag_tables(w.cp, 1, w.chunk_len)
+    cache = {}
+    ref_out, ref_lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV, kv_cache=cache)
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    for where in ("copy", "main"):
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side if where == "copy" else main):
+            torch.cuda._sleep(20_000_000)   # bounded spin, ~10 ms
+        out, lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV, copy_stream=side, kv_cache=cache)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), where
