@@ -1,0 +1,236 @@
+"""Benchmark: one CP rank's share of causal ring attention on one MI355X.
+
+A step is one cp_ring_attn_fwd call: every ring step of the rank's share
+(staging copy of the next K/V block on a side stream, attention of the local
+queries against the current block, fused log-sum-exp merge, bf16 output).
+Default workload: S = 32768, context-parallel size 8, rank 0, B = 1, H = 32,
+D = 128 (local queries 4096 tokens in two zigzag chunks of 2048, eight ring
+steps of 4096 keys).  Inputs are seeded synthetic bf16 ~ N(0, 1), resident in
+HBM (all eight ranks' K/V blocks) before timing starts.
+
+Prints one JSON line.  The metric is causal-effective TFLOP/s: 4*D*B*H times
+the number of visible (query, key) pairs of the rank's share, per second.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+
+
+def visible_pairs(q_tab, kv_tabs):
+    """Visible (query, key) pairs of one (batch, head), summed over ring steps and chunk pairs.
+
+    For a query chunk starting at qs (length Lq) and a key chunk at ks (length
+    Lk), query position p sees min(max(p - ks + 1, 0), Lk) keys.
+    """
+    def S(n, Lk):   # sum_{x=1..n} min(x, Lk)
+        if n <= 0:
+            return 0
+        return n * (n + 1) // 2 if n <= Lk else Lk * (Lk + 1) // 2 + (n - Lk) * Lk
+
+    total = 0
+    Lq = q_tab.chunk_len
+    for t in kv_tabs:
+        for qs in q_tab.starts():
+            for ks in t.starts():
+                total += S(qs - ks + Lq, t.chunk_len) - S(qs - ks, t.chunk_len)
+    return total
+
+
+def cpu_baseline(w, rank, budget_s, Q, K, V):
+    """Time the fp64 oracle on a bounded sample of the same share (rows of head 0)."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    # head 0 of the same inputs, rows of the rank's share; add rows until the budget is used
+    pos = oracle.local_positions(w.S, w.cp, rank)
+    q, k, v = (oracle.to_f64(x[0, 0]) for x in (Q, K, V))
+    # warm up BLAS threads
+    oracle.causal_attention_rows(q, k, v, pos[:8], w.scale)
+    order = np.random.default_rng(0).permutation(len(pos))
+    done_rows, pairs, t0 = 0, 0, time.perf_counter()
+    step = 256
+    while done_rows < len(pos) and time.perf_counter() - t0 < budget_s:
+        rows = np.sort(pos[order[done_rows:done_rows + step]])
+        oracle.causal_attention_rows(q, k, v, rows, w.scale)
+        pairs += int((rows + 1).sum())
+        done_rows += len(rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * pairs
+    info = workloads.host_info()
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": f"{done_rows} of {len(pos)} query rows of head 0 (rank {rank}, random order), "
+                  f"{pairs} visible pairs in {dt:.1f} s; {info['cpu_model']}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="s32k_cp8")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "step_kernel_traffic.json"))
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's rank share only; multi-GPU runs are not part of this "
+              "build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads
+    import long_sequence_causal_cp_amd as cp
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cp.load_library()
+    dev = torch.device("cuda:0")
+    w = workloads.get(args.workload)
+    L, N, r = w.chunk_len, w.cp, args.rank
+    Q, K, V = workloads.make_qkv(w)
+
+    def gather(x, t):
+        idx = torch.cat([torch.arange(s, s + t.chunk_len) for s in t.starts()])
+        return x.index_select(2, idx).contiguous().to(dev)
+
+    q_tab = cp.cp_zigzag_chunks(N, r, L, 0)[0]
+    rank_kv = {}
+    for src in range(N):       # every rank's K/V block resident in HBM
+        t = cp.cp_zigzag_chunks(N, src, L, 0)[0]
+        rank_kv[src] = (gather(K, t), gather(V, t), t)
+    kv_tabs, ks, vs = [], [], []
+    for j in range(N):
+        src = (r - j) % N
+        kk, vv, t = rank_kv[src]
+        ks.append(kk)
+        vs.append(vv)
+        kv_tabs.append(t)
+    q = gather(Q, q_tab)
+    B, H, Sq, D = q.shape
+    Skv = ks[0].shape[2]
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    ws = torch.empty(cp.cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq), dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cp.cp_ring_attn_fwd(q, q_tab, ks, vs, kv_tabs, out, lse, w.scale, ws, stream=stream,
+                            copy_stream=copy_stream)
+
+    pairs = visible_pairs(q_tab, kv_tabs)
+    flops = 4.0 * D * B * H * pairs
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {w.describe()} rank {r}: warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    # timed region: K steps, HIP events on the launch stream, step kernels timed by the library
+    cp.cp_profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = cp.cp_profile_read(8192)
+    cp.cp_profile_enable(False)
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    n_launch = len(kern_ms)
+    assert n_launch == args.steps * N, (n_launch, args.steps * N)
+    avg_kernel_ms = statistics.fmean(kern_ms)
+    per_launch_flops = flops / N
+    achieved = per_launch_flops / (avg_kernel_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                tj = json.load(f)
+            if tj.get("workload") == w.name:
+                traffic = tj.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    # spot check a few rows against the oracle (outside the timed region)
+    import oracle
+    pos = oracle.local_positions(w.S, N, r)
+    rows = np.array([0, L - 1, L, 2 * L - 1])
+    ro, rl = oracle.causal_attention_rows(oracle.to_f64(Q[0, 0]), oracle.to_f64(K[0, 0]),
+                                          oracle.to_f64(V[0, 0]), pos[rows], w.scale)
+    eo = float(np.max(np.abs(out[0, 0, rows].float().cpu().numpy() - ro)))
+    el = float(np.max(np.abs(lse[0, 0, rows].cpu().numpy() - rl)))
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.1f} TFLOP/s; "
+          f"step kernel avg {avg_kernel_ms:.4f} ms over {n_launch} launches; spot check "
+          f"max|dout| {eo:.2e} max|dlse| {el:.2e}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(w, r, args.cpu_budget, Q, K, V)
+
+    res = {
+        "metric": "causal-effective attention TFLOP/s per CP-rank share; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": f"{w.name}: causal ring attention, one rank's share (rank {r} of cp={N}), "
+                        f"B={B} H={H} D={D} S={w.S}, zigzag chunks of {L}, {N} ring steps of {Skv} keys",
+            "seq_len": w.S, "cp": N, "rank": r, "B": B, "H": H, "D": D,
+            "visible_pairs_per_head": pairs, "flop_per_step": flops,
+            "wall_s_timed": round(wall, 4),
+        },
+        "roofline": {
+            "kernel": "step_kernel<128,4> (QK^T, mask, online softmax, PV, fused LSE merge)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "launches": n_launch,
+            "avg_launch_ms": round(avg_kernel_ms, 5),
+        },
+        "cpu_baseline": cpu,
+        "check": {"max_abs_dout": eo, "max_abs_dlse": el},
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

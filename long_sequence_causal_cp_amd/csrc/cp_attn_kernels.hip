@@ -73,8 +73,10 @@ __device__ __forceinline__ int v_off(int r, int c) {
   return r * (D * 2) + ((c ^ v_swz<D>(r)) << 4);
 }
 
+// Four-wave workgroups are built for two waves per SIMD (at most 256 VGPRs),
+// so two workgroups share a CU and one's softmax overlaps the other's MFMAs.
 template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64) step_kernel(const StepArgs a) {
+__global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) step_kernel(const StepArgs a) {
   constexpr int BM = 32 * NW;
   constexpr int NT = NW * 64;
   constexpr int NC = D / 8;    // 16-byte chunks per row
