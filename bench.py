@@ -50,7 +50,11 @@ def visible_pairs(q_tab, kv_tabs):
 
 
 def cpu_baseline(w, rank, budget_s, Q, K, V):
-    """Time the fp64 oracle on a bounded sample of the same share (rows of head 0)."""
+    """Time the fp64 oracle on a bounded sample of the same share.
+
+    The sample is the rank's full set of query rows for as many (batch, head)
+    pairs as fit in ``budget_s`` seconds (at least one head), taken in order.
+    """
     import numpy as np
     import oracle
     import workloads
@@ -59,27 +63,44 @@ def cpu_baseline(w, rank, budget_s, Q, K, V):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    # head 0 of the same inputs, rows of the rank's share; add rows until the budget is used
     pos = oracle.local_positions(w.S, w.cp, rank)
-    q, k, v = (oracle.to_f64(x[0, 0]) for x in (Q, K, V))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     # warm up BLAS threads
-    oracle.causal_attention_rows(q, k, v, pos[:8], w.scale)
-    order = np.random.default_rng(0).permutation(len(pos))
-    done_rows, pairs, t0 = 0, 0, time.perf_counter()
-    step = 256
-    while done_rows < len(pos) and time.perf_counter() - t0 < budget_s:
-        rows = np.sort(pos[order[done_rows:done_rows + step]])
-        oracle.causal_attention_rows(q, k, v, rows, w.scale)
-        pairs += int((rows + 1).sum())
-        done_rows += len(rows)
+    oracle.causal_attention_rows(oracle.to_f64(Q[0, 0]), oracle.to_f64(K[0, 0]), oracle.to_f64(V[0, 0]),
+                                 pos[:8], w.scale)
+    done, pairs, t0 = 0, 0, time.perf_counter()
+    for b, h in heads:
+        q, k, v = (oracle.to_f64(x[b, h]) for x in (Q, K, V))
+        oracle.causal_attention_rows(q, k, v, pos, w.scale)
+        pairs += int((pos + 1).sum())
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
     flops = 4.0 * w.D * pairs
     info = workloads.host_info()
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-        "sample": f"{done_rows} of {len(pos)} query rows of head 0 (rank {rank}, random order), "
-                  f"{pairs} visible pairs in {dt:.1f} s; {info['cpu_model']}",
+        "sample": f"all {len(pos)} query rows of rank {rank} for {done} of {len(heads)} (batch, head) "
+                  f"pairs: {pairs} visible pairs in {dt:.1f} s; {info['cpu_model']}",
     }
+
+
+def copy_probe(mib, reps):
+    """Plain device copy of ``mib`` MiB (torch copy kernel), for counter calibration.
+
+    Each launch reads and writes exactly mib MiB; FETCH_SIZE / WRITE_SIZE of
+    this kernel give the counters' scale against known bytes.
+    """
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": reps}),
+          flush=True)
 
 
 def main():
@@ -90,12 +111,18 @@ def main():
     ap.add_argument("--workload", default="s32k_cp8")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "step_kernel_traffic.json"))
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "step_kernel_s32k_cp8_traffic.json"))
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's rank share only; multi-GPU runs are not part of this "
               "build (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib, args.steps)
+        return
 
     import numpy as np
     import torch
@@ -168,14 +195,17 @@ def main():
     avg_kernel_ms = statistics.fmean(kern_ms)
     per_launch_flops = flops / N
     achieved = per_launch_flops / (avg_kernel_ms * 1e-3) / 1e12
+    # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counters, only if they
+    # were taken on this workload and on the kernel source that is built now
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
+            from long_sequence_causal_cp_amd.prof_summary import kernel_source_sha256
             with open(args.traffic_json) as f:
                 tj = json.load(f)
-            if tj.get("workload") == w.name:
-                traffic = tj.get("bytes_per_launch")
-        except (OSError, ValueError):
+            if tj.get("workload") == w.name and tj.get("kernel_source_sha256") == kernel_source_sha256():
+                traffic = round(tj["bytes_per_launch"])
+        except (OSError, ValueError, KeyError):
             traffic = None
 
     # spot check a few rows against the oracle (outside the timed region)

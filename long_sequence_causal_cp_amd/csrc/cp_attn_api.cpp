@@ -150,9 +150,10 @@ hipError_t launch_step_timed(const StepArgs& a, int D, hipStream_t s) {
     if (p.enabled && p.used < kMaxTimed) {
       if (p.used == p.ev.size()) {
         hipEvent_t e0, e1;
-        hipError_t e = hipEventCreate(&e0);
+        // device-scope release: the timed kernels only need ordering on the GPU
+        hipError_t e = hipEventCreateWithFlags(&e0, hipEventReleaseToDevice);
         if (e != hipSuccess) return e;
-        e = hipEventCreate(&e1);
+        e = hipEventCreateWithFlags(&e1, hipEventReleaseToDevice);
         if (e != hipSuccess) return e;
         p.ev.emplace_back(e0, e1);
       }
@@ -179,7 +180,8 @@ cp_status_t get_events(int n, std::vector<hipEvent_t>& out) {
   auto& pool = g_pools[dev];
   while ((int)pool.size() < n) {
     hipEvent_t ev;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    // ordering between two streams of one device needs no system-scope fence
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
     pool.push_back(ev);
   }

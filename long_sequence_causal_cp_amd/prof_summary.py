@@ -1,0 +1,117 @@
+"""Summaries of rocprofv3 CSV output for the step kernel (text + traffic JSON).
+
+Usage (after rocprofv3 runs with ``--output-format csv``):
+
+  python -m long_sequence_causal_cp_amd.prof_summary stats KERNEL_STATS_CSV --cmd "..."
+  python -m long_sequence_causal_cp_amd.prof_summary traffic --fetch F.csv --write W.csv \
+      --copy-fetch CF.csv --copy-write CW.csv --workload s32k_cp8 --cmd-fetch "..." ...
+
+``traffic`` calibrates the two L2-to-HBM byte counters (FETCH_SIZE and
+WRITE_SIZE, KiB per dispatch) against a plain device copy of known size: the
+factor is known bytes / counted bytes for that copy.  The step kernel's
+per-launch HBM traffic is then the mean over its dispatches of
+factor_fetch * FETCH_SIZE + factor_write * WRITE_SIZE.  The JSON records the
+SHA-256 of the kernel source it was measured on, so that a benchmark can
+refuse to report traffic taken on a different kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(HERE, "csrc", "cp_attn_kernels.hip")
+
+
+def kernel_source_sha256(path: str = KERNEL_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(path, counter, name_substr):
+    vals = []
+    for r in _rows(path):
+        if r["Counter_Name"] == counter and name_substr in r["Kernel_Name"]:
+            vals.append((int(r["Dispatch_Id"]), int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return vals
+
+
+def stats_text(stats_csv: str, cmd: str, top: int = 6) -> str:
+    rows = _rows(stats_csv)
+    out = [f"command: {cmd}", "", f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} "
+           f"{'max_us':>10s} {'pct':>6s}"]
+    for r in rows[:top]:
+        name = r["Name"]
+        name = name if len(name) <= 70 else name[:67] + "..."
+        out.append(f"{name:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                   f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                   f"{float(r['Percentage']):6.2f}")
+    return "\n".join(out) + "\n"
+
+
+def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, kernel="step_kernel"):
+    cf = [v for _, _, v in _per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")]
+    cw = [v for _, _, v in _per_dispatch(copy_write_csv, "WRITE_SIZE", "copyBuffer")]
+    if not cf or not cw:
+        raise SystemExit("no copy-probe dispatches found")
+    f_fetch = copy_bytes / (statistics.fmean(cf) * 1024.0)
+    f_write = copy_bytes / (statistics.fmean(cw) * 1024.0)
+    kf = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
+    kw = _per_dispatch(write_csv, "WRITE_SIZE", kernel)
+    if not kf or not kw:
+        raise SystemExit(f"no {kernel} dispatches found")
+    fetch_b = statistics.fmean(v for _, _, v in kf) * 1024.0 * f_fetch
+    write_b = statistics.fmean(v for _, _, v in kw) * 1024.0 * f_write
+    by_grid = {}
+    for _, g, v in kf:
+        by_grid.setdefault(g, [[], []])[0].append(v)
+    for _, g, v in kw:
+        by_grid.setdefault(g, [[], []])[1].append(v)
+    grids = {str(g): {"dispatches": len(a), "fetch_bytes": statistics.fmean(a) * 1024.0 * f_fetch,
+                      "write_bytes": statistics.fmean(b) * 1024.0 * f_write}
+             for g, (a, b) in sorted(by_grid.items()) if a and b}
+    return {
+        "factor_fetch": f_fetch, "factor_write": f_write,
+        "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+        "bytes_per_launch": fetch_b + write_b, "dispatches": len(kf), "by_grid_size": grids,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="sub", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True, help="bytes the copy probe reads (= writes)")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--commands", required=True, help="the rocprofv3 commands, one string")
+    t.add_argument("--json-out", required=True)
+    a = ap.parse_args(argv)
+    if a.sub == "stats":
+        sys.stdout.write(stats_text(a.csv, a.cmd))
+        return
+    res = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes)
+    res.update({"workload": a.workload, "kernel_source_sha256": kernel_source_sha256(), "commands": a.commands})
+    with open(a.json_out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    main()
