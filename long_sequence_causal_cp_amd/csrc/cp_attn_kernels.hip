@@ -58,38 +58,89 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS layouts of one 64-key tile, row-major [key][d] bf16, 16-byte chunks
-// XOR-swizzled so that the MFMA operand reads hit distinct banks.
-template <int D>
-__device__ __forceinline__ int k_off(int r, int c) {
-  return r * (D * 2) + ((c ^ (r & (D / 8 - 1))) << 4);
+// LDS layout of a K tile (64 keys x D): D/16 column blocks of 16 d-values;
+// block st holds the 64 rows at 32 B each, and a row's two 16-B halves are
+// swapped when bits 2 and 3 of the row differ.  The QK^T operand read of lane
+// (row r, half g) in block st is then one base address plus the immediate
+// st*2048, and any 8 (or 16) consecutive lanes hit distinct 16-B bank groups.
+__device__ __forceinline__ int k_half_swap(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+__device__ __forceinline__ int k_lds_off(int r, int st, int g) {
+  return st * 2048 + r * 32 + ((g ^ k_half_swap(r)) << 4);
 }
+// LDS layout of a V tile: row-major [key][d] bf16, 16-byte chunks XOR-swizzled
+// by the row so that the transposed reads hit distinct banks.
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
   return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
-template <int D>
-__device__ __forceinline__ int v_off(int r, int c) {
-  return r * (D * 2) + ((c ^ v_swz<D>(r)) << 4);
+
+// One direct-to-LDS load: each lane fetches 16 bytes at `src`; lane i's
+// bytes land at LDS address `lds_dst` + 16 i (`lds_dst` wave-uniform, in M0).
+// Issued as inline assembly so that the compiler's LDS-counter bookkeeping is
+// not made conservative by it: with a compiler-visible LDS DMA in flight every
+// ds_read wait becomes lgkmcnt(0).  Completion is tracked by hand instead:
+// wait_vmem_all() before the barrier that publishes the tile.  No other code
+// in this file uses M0.
+__device__ __forceinline__ void global_to_lds_16(const void* src, unsigned char* lds_dst) {
+  const unsigned m0 = (unsigned)(uintptr_t)LDS_PTR(void, lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
+}
+
+// Global -> LDS copy of one 64-key tile with the direct-to-LDS load: every
+// wave instruction j writes LDS bytes [1024 j, 1024 j + 1024), lane i the 16
+// bytes at 1024 j + 16 i, so each layout is produced by choosing which global
+// 16-B chunk lane i fetches.
+template <int D, int NW, bool kIsK>
+__device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ rows, unsigned char* lds_buf, int wave_u,
+                                            int lane) {
+  constexpr int NC = D / 8;     // 16-B chunks per row = 1 KiB blocks per tile
+  constexpr int LPW = NC / NW;  // load instructions per wave per tile
+  static_assert(LPW * NW == NC, "tile load must divide evenly");
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int j = i * NW + wave_u;
+    int r, c;
+    if constexpr (kIsK) {
+      r = 32 * (j & 1) + (lane >> 1);
+      c = 2 * (j >> 1) + ((lane & 1) ^ k_half_swap(r));
+    } else {
+      const int slot = j * 64 + lane;
+      r = slot / NC;
+      c = (slot % NC) ^ v_swz<D>(r);
+    }
+    global_to_lds_16(rows + r * D + 8 * c, lds_buf + j * 1024);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  // s_waitcnt vmcnt(0): every global load this wave issued, including the
+  // direct-to-LDS ones, has landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 // Four-wave workgroups are built for two waves per SIMD (at most 256 VGPRs),
-// so two workgroups share a CU and one's softmax overlaps the other's MFMAs.
+// so two workgroups share a CU.  Each wave runs a software pipeline over
+// 32-key sub-tiles u (two per 64-key LDS tile): sub-iteration u computes the
+// exponentials of sub-tile u while its MFMAs are QK^T of sub-tile u+1 and PV
+// of sub-tile u-1, neither of which depends on that sub-iteration's VALU
+// work, so the two streams interleave freely.
 template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) step_kernel(const StepArgs a) {
+__global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) step_kernel(const StepArgs a) {
   constexpr int BM = 32 * NW;
-  constexpr int NT = NW * 64;
-  constexpr int NC = D / 8;    // 16-byte chunks per row
   constexpr int NS = D / 16;   // k-steps of the QK^T MFMA
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
   constexpr int TB = kTileKeys * D * 2;
-  constexpr int CPT = kTileKeys * NC / NT;  // chunks per thread per tile
-  static_assert(CPT * NT == kTileKeys * NC, "tile load must divide evenly");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TB];
+  // two K and two V tile buffers, separate objects so that the compiler can
+  // tell the direct-to-LDS writes of one buffer from the reads of another
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int g = lane >> 5;
   const int lq = lane & 31;
 
@@ -114,7 +165,7 @@ __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) step_kernel(const St
   const int q_pos0 = a.q_start[qc] + rbi * BM;
   const int q_posmax = q_pos0 + BM - 1;
   const int qw_local = q_local0 + wave * 32;
-  const int qw_pos = q_pos0 + wave * 32;
+  const int qw_pos = q_pos0 + wave_u * 32;
   const size_t bh_q = (size_t)bh * a.Sq;
   const size_t bh_kv = (size_t)bh * a.Skv;
 
@@ -132,13 +183,36 @@ __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) step_kernel(const St
     n_vis[c] = nv;
     T += nv;
   }
-  auto tile_at = [&](int it, int& krow, int& kpos) {
-    int c = 0;
+  // Tiles are visited chunk by chunk.  A cursor names one tile: its chunk,
+  // how many visible tiles of that chunk remain from it, its row in the
+  // local K/V buffer and its absolute key position.  The chunk table is only
+  // read with constant indices, so it stays in scalar registers.
+  int kv_start[kMaxChunks];
 #pragma unroll
-    for (int cc = 0; cc < kMaxChunks - 1; ++cc)
-      if (c == cc && it >= n_vis[cc]) { it -= n_vis[cc]; c = cc + 1; }
-    krow = c * a.kv_chunk_len + it * kTileKeys;
-    kpos = a.kv_start[c] + it * kTileKeys;
+  for (int c = 0; c < kMaxChunks; ++c) kv_start[c] = a.kv_start[c];
+  struct Cursor {
+    int c, left, krow, kpos;
+  };
+  // first visible tile of a chunk after chunk `after` (c = kMaxChunks if none)
+  auto chunk_after = [&](int after) {
+    Cursor t{kMaxChunks, 0, 0, 0};
+#pragma unroll
+    for (int c = kMaxChunks - 1; c >= 0; --c)
+      if (c > after && n_vis[c] > 0) t = Cursor{c, n_vis[c], c * a.kv_chunk_len, kv_start[c]};
+    return t;
+  };
+  auto next_tile = [&](Cursor t) {
+    t.left -= 1;
+    t.krow += kTileKeys;
+    t.kpos += kTileKeys;
+    if (t.left <= 0) t = chunk_after(t.c);  // rare: chunk boundary
+    return t;
+  };
+  auto load_k = [&](const Cursor& t, unsigned char* buf) {
+    tile_to_lds<D, NW, true>(a.k + (bh_kv + t.krow) * D, buf, wave_u, lane);
+  };
+  auto load_v = [&](const Cursor& t, unsigned char* buf) {
+    tile_to_lds<D, NW, false>(a.v + (bh_kv + t.krow) * D, buf, wave_u, lane);
   };
 
   // Q^T fragments: lane holds Q[row lq][16s + 8g .. +8]
@@ -156,128 +230,177 @@ __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) step_kernel(const St
   float l_lane = 0.f;       // this lane's share of the row sum
 
   // per-lane constant parts of the LDS reads
+  const int k_base = k_lds_off(lq, 0, g);
   const int j16 = lane & 15;
   const int G = lane >> 4;
-  const int tr_row = 4 * g + (j16 >> 2);               // + 16t (+8)
+  const int tr_row = 4 * g + (j16 >> 2);  // + 16t (+8)
   const int tr_swz = v_swz<D>(tr_row);
   const int tr_colbyte = 8 * (j16 & 1);
-  int tr_chunk[NDB];
+  int tr_off[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) tr_chunk[db] = 4 * db + 2 * (G & 1) + ((j16 & 3) >> 1);
+  for (int db = 0; db < NDB; ++db)
+    tr_off[db] = tr_row * (D * 2) + (((4 * db + 2 * (G & 1) + ((j16 & 3) >> 1)) ^ tr_swz) << 4) + tr_colbyte;
 
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int it) {
-    int krow, kpos;
-    tile_at(it, krow, kpos);
-    const uint16_t* kb = a.k + (bh_kv + krow) * D;
-    const uint16_t* vb = a.v + (bh_kv + krow) * D;
+  // S^T of one 32-key sub-tile: K rows [32h, 32h+32) of the tile in `kb`
+  auto qk_sub = [&](const unsigned char* kb, int h) {
+    f32x16 s = {};
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      const int r = idx / NC, c = idx % NC;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kb + r * D + 8 * c);
-      vreg[i] = *reinterpret_cast<const u32x4*>(vb + r * D + 8 * c);
+    for (int st = 0; st < NS; ++st) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + k_base + st * 2048 + h * 1024);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s, 0, 0, 0);
     }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* kl = lds + buf * 2 * TB;
-    unsigned char* vl = kl + TB;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      const int r = idx / NC, c = idx % NC;
-      *reinterpret_cast<u32x4*>(kl + k_off<D>(r, c)) = kreg[i];
-      *reinterpret_cast<u32x4*>(vl + v_off<D>(r, c)) = vreg[i];
-    }
+    return s;
   };
 
-  auto compute_tile = [&](int buf, int kpos, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    const unsigned char* kl = lds + buf * 2 * TB;
-    const unsigned char* vl = kl + TB;
-    // S^T = K Q^T over two 32-key blocks
-    f32x16 sacc[2];
+  // The branch-free body of sub-iteration u.
+  //   exp:  row max of s_cur (scores of sub-tile u) -> lazy max update -> 16
+  //         exponentials per lane, their row sum and bf16 packing into p_cur;
+  //   QK:   s_nxt = K Q^T of sub-tile u+1, rows [32 hn, +32) of `kn` (kQK);
+  //   PV:   O^T += V^T P^T of sub-tile u-1, rows [32 hp, +32) of `vp` (kPV).
+  // Returns the factor the output must be scaled by once PV(u-1) is in.
+  auto body = [&](const f32x16& s_cur, f32x16& s_nxt, bf16x8 (&p_cur)[2], const bf16x8 (&p_prev)[2],
+                  const unsigned char* kn, int hn, const unsigned char* vp, int hp, auto exp_tag, auto qk_tag,
+                  auto pv_tag) {
+    constexpr bool kExp = decltype(exp_tag)::value;
+    constexpr bool kQK = decltype(qk_tag)::value;
+    constexpr bool kPV = decltype(pv_tag)::value;
+    // MFMA stream: QK^T and PV alternate so that consecutive MFMAs never
+    // share an accumulator
+    if constexpr (kQK) s_nxt = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      const int r = 32 * kb + lq;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + k_off<D>(r, 2 * s + g));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+    for (int i = 0; i < NS; ++i) {
+      if constexpr (kQK) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kn + k_base + i * 2048 + hn * 1024);
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i], s_nxt, 0, 0, 0);
+      }
+      if constexpr (kPV) {
+        if (i < 2 * NDB) {
+          const int t = i / NDB, db = i % NDB;
+          const unsigned char* base = vp + (32 * hp + 16 * t) * (D * 2) + tr_off[db];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, base));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, base + 8 * (D * 2)));
+          const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, p_prev[t], oacc[db], 0, 0, 0);
+        }
       }
     }
-    if constexpr (kMasked) {
-      const int qpos = qw_pos + lq;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kp = kpos + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (kp > qpos) sacc[kb][r] = neg_inf();
-        }
-    }
+    if constexpr (!kExp) return 1.f;
+    // VALU stream
     float mx = neg_inf();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
     mx = xhalf_max(mx) * a.scale_log2;
-    const bool need = mx > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_lane *= alpha;
+    const float m_new = (mx > m_run + kRescaleThreshold) ? mx : m_run;
+    const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    const float negm = (m_run == neg_inf()) ? 0.f : -m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[8 * t + e], a.scale_log2, negm));
+        lsum += p;
+        p_cur[t][e] = (__bf16)p;
+      }
+    l_lane = __builtin_fmaf(l_lane, alpha, lsum);
+    // interleave: each MFMA followed by its share of LDS reads and VALU work
+    constexpr int kMfma = (kQK ? NS : 0) + (kPV ? 2 * NDB : 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    return alpha;
+  };
+
+  auto mask = [&](f32x16& s, int kpos) {
+    const int qpos = qw_pos + lq;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kp = kpos + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (kp > qpos) s[r] = neg_inf();
+    }
+  };
+  // Sub-iteration u: mask S(u) (first key at kpos) if it crosses this wave's
+  // diagonal, run the body, then (rarely) rescale the output once PV(u-1)
+  // is in.
+  auto sub = [&](int kpos, f32x16& s_cur, f32x16& s_nxt, bf16x8 (&p_cur)[2], const bf16x8 (&p_prev)[2],
+                 const unsigned char* kn, int hn, const unsigned char* vp, int hp, auto exp_tag, auto qk_tag,
+                 auto pv_tag) {
+    if constexpr (decltype(exp_tag)::value) {
+      if (kpos + 31 > qw_pos) mask(s_cur, kpos);
+    }
+    const float alpha = body(s_cur, s_nxt, p_cur, p_prev, kn, hn, vp, hp, exp_tag, qk_tag, pv_tag);
+    if (__any(alpha != 1.f)) {  // rare: the running max moved; P(u) is on the new scale
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    const float negm = (m_run == neg_inf()) ? 0.f : -m_run;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, negm));
-        sacc[kb][r] = p;
-        l_lane += p;
-      }
-    // O^T += V^T P^T, four k-steps of 16 keys
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[t >> 1][8 * (t & 1) + e];
-      const int row1 = 16 * t + tr_row;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int cb = ((tr_chunk[db] ^ tr_swz) << 4) + tr_colbyte;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vl + row1 * (D * 2) + cb));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vl + (row1 + 8) * (D * 2) + cb));
-        const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb, oacc[db], 0, 0, 0);
-      }
-    }
+  };
+  // Cursors at pair n: tm = tile n, tv = tile n+1, tk = tile n+2.
+  Cursor tm = chunk_after(-1);
+  Cursor tv = next_tile(tm);
+  Cursor tk = next_tile(tv);
+  // Top of tile pair n: K(n+1) and V(n) have landed and every wave is done
+  // with K(n) and V(n-1); start loading K(n+2) and V(n+1) into those buffers.
+  auto barrier_and_prefetch = [&](int n, unsigned char* k_dst, unsigned char* v_dst) {
+    wait_vmem_all();
+    __syncthreads();
+    if (n + 2 < T) load_k(tk, k_dst);
+    if (n + 1 < T) load_v(tv, v_dst);
+  };
+  auto advance = [&]() {
+    tm = tv;
+    tv = tk;
+    tk = next_tile(tk);
   };
 
+  // Sub-tile u is half (u & 1) of tile u >> 1; K(t) and V(t) live in buffer
+  // t & 1.  Sub-iteration u uses registers sa/pa for S(u)/P(u) when u is
+  // even and sb/pb when u is odd.  Tile pair n holds sub-iterations 2n+1
+  // (QK^T of tile n+1 half 0, PV of tile n half 0) and 2n+2 (halves 1).
+  using Yes = std::true_type;
+  using No = std::false_type;
   if (T > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_k(tm, lds_k0);
+    if (T > 1) load_k(tv, lds_k1);
+    load_v(tm, lds_v0);
+    wait_vmem_all();
     __syncthreads();
-    for (int it = 0; it < T; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < T) load_tile(it + 1);
-      int krow, kpos;
-      tile_at(it, krow, kpos);
-      if (kpos <= qw_pos + 31) {  // this wave sees at least one key of the tile
-        if (kpos + kTileKeys - 1 > qw_pos)
-          compute_tile(buf, kpos, std::true_type{});
-        else
-          compute_tile(buf, kpos, std::false_type{});
-      }
-      if (it + 1 < T) store_tile(buf ^ 1);
-      __syncthreads();
+    f32x16 sa, sb;
+    bf16x8 pa[2], pb[2];
+    sa = qk_sub(lds_k0, 0);
+    sub(tm.kpos, sa, sb, pa, pb, lds_k0, 1, lds_v0, 0, Yes{}, Yes{}, No{});
+    int n = 0;
+    // full pairs n = 0 .. T-2, two per trip (even n, then odd n)
+    for (; n + 2 < T; n += 2) {
+      barrier_and_prefetch(n, lds_k0, lds_v1);
+      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k1, 0, lds_v0, 0, Yes{}, Yes{}, Yes{});
+      sub(tv.kpos, sa, sb, pa, pb, lds_k1, 1, lds_v0, 1, Yes{}, Yes{}, Yes{});
+      advance();
+      barrier_and_prefetch(n + 1, lds_k1, lds_v0);
+      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k0, 0, lds_v1, 0, Yes{}, Yes{}, Yes{});
+      sub(tv.kpos, sa, sb, pa, pb, lds_k0, 1, lds_v1, 1, Yes{}, Yes{}, Yes{});
+      advance();
+    }
+    if (n + 1 < T) {
+      // n = T-2 (even): one more full pair, then the tail pair T-1 (odd, V in v1)
+      barrier_and_prefetch(n, lds_k0, lds_v1);
+      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k1, 0, lds_v0, 0, Yes{}, Yes{}, Yes{});
+      sub(tv.kpos, sa, sb, pa, pb, lds_k1, 1, lds_v0, 1, Yes{}, Yes{}, Yes{});
+      advance();
+      barrier_and_prefetch(n + 1, lds_k1, lds_v0);
+      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k0, 0, lds_v1, 0, Yes{}, No{}, Yes{});
+      sub(0, sa, sb, pa, pb, lds_k0, 0, lds_v1, 1, No{}, No{}, Yes{});
+    } else {
+      // n = T-1 (even): the tail pair, V in v0
+      barrier_and_prefetch(n, lds_k1, lds_v1);
+      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k1, 0, lds_v0, 0, Yes{}, No{}, Yes{});
+      sub(0, sa, sb, pa, pb, lds_k1, 0, lds_v0, 1, No{}, No{}, Yes{});
     }
   }
 
@@ -390,20 +513,24 @@ __global__ void __launch_bounds__(256) merge_kernel(float* o_acc, float* lse_acc
 
 }  // namespace
 
-int step_block_rows(int q_chunk_len) { return (q_chunk_len % 128 == 0) ? 128 : 64; }
+int step_block_rows(int q_chunk_len) {
+  return (q_chunk_len % 256 == 0) ? 256 : (q_chunk_len % 128 == 0) ? 128 : 64;
+}
 
 hipError_t launch_step(const StepArgs& a, int D, hipStream_t stream) {
   const int bm = step_block_rows(a.q_chunk_len);
   const long long grid = (long long)a.n_order * a.rb_per_chunk * a.BH;
   if (grid <= 0) return hipSuccess;
-  if (D == 128 && bm == 128)
-    hipLaunchKernelGGL((step_kernel<128, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a);
-  else if (D == 128)
-    hipLaunchKernelGGL((step_kernel<128, 2>), dim3((unsigned)grid), dim3(128), 0, stream, a);
-  else if (bm == 128)
-    hipLaunchKernelGGL((step_kernel<64, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((step_kernel<64, 2>), dim3((unsigned)grid), dim3(128), 0, stream, a);
+  const dim3 g((unsigned)grid), blk((unsigned)(2 * bm));  // one wave per 32 rows
+  if (D == 128) {
+    if (bm == 256) hipLaunchKernelGGL((step_kernel<128, 8>), g, blk, 0, stream, a);
+    else if (bm == 128) hipLaunchKernelGGL((step_kernel<128, 4>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((step_kernel<128, 2>), g, blk, 0, stream, a);
+  } else {
+    if (bm == 256) hipLaunchKernelGGL((step_kernel<64, 8>), g, blk, 0, stream, a);
+    else if (bm == 128) hipLaunchKernelGGL((step_kernel<64, 4>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((step_kernel<64, 2>), g, blk, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
