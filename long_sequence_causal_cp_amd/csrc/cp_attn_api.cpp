@@ -371,10 +371,8 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
 
   auto stage = [&](int j) -> cp_status_t {  // copy step j's block into slot j%2 on copy_stream
     if (j >= 3) HIP_TRY(hipStreamWaitEvent(copy_stream, released[j - 2], 0), "hipStreamWaitEvent");
-    HIP_TRY(hipMemcpyAsync(slot_k[j & 1], k_steps[j], kv_bytes, hipMemcpyDeviceToDevice, copy_stream),
-            "hipMemcpyAsync(K)");
-    HIP_TRY(hipMemcpyAsync(slot_v[j & 1], v_steps[j], kv_bytes, hipMemcpyDeviceToDevice, copy_stream),
-            "hipMemcpyAsync(V)");
+    HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k[j & 1], v_steps[j], slot_v[j & 1], kv_bytes, copy_stream),
+            "staging copy launch");
     HIP_TRY(hipEventRecord(copied[j], copy_stream), "hipEventRecord");
     return CP_OK;
   };

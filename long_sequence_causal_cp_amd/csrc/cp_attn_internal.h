@@ -45,6 +45,11 @@ int step_block_rows(int q_chunk_len);
 // Launch the step kernel; `grid` = n_order * rb_per_chunk * BH workgroups.
 hipError_t launch_step(const StepArgs& a, int D, hipStream_t stream);
 
+// Copy one ring step's K and V blocks (`bytes` each, a multiple of 16) into a
+// staging slot on `stream` (the copy stream of the ring driver).
+hipError_t launch_stage_copy(const void* k_src, void* k_dst, const void* v_src, void* v_dst, size_t bytes,
+                             hipStream_t stream);
+
 // Standalone merge kernel.
 hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
                         uint16_t* out, int64_t rows, int D, hipStream_t stream);

@@ -125,7 +125,7 @@ __device__ __forceinline__ void wait_vmem_all() {
 // of sub-tile u-1, neither of which depends on that sub-iteration's VALU
 // work, so the two streams interleave freely.
 template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) step_kernel(const StepArgs a) {
+__device__ __forceinline__ void step_body(const StepArgs& a) {
   constexpr int BM = 32 * NW;
   constexpr int NS = D / 16;   // k-steps of the QK^T MFMA
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
@@ -456,6 +456,19 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) step_kernel(con
     }
 }
 
+// Entry points.  Eight-wave workgroups (256 rows) run two waves per SIMD and
+// are held to 248 VGPRs, so that 16 registers per SIMD stay free for the
+// waves of a concurrent staging copy on the copy stream; the smaller shapes
+// (chunk lengths that are not multiples of 256) run one wave per SIMD.
+template <int D>
+__global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_num_vgpr(124))) step_kernel_256(const StepArgs a) {
+  step_body<D, 8>(a);
+}
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) step_kernel_small(const StepArgs a) {
+  step_body<D, NW>(a);
+}
+
 // ---- standalone log-sum-exp merge, HBM-bound elementwise pass ----
 __global__ void __launch_bounds__(256) merge_kernel(float* o_acc, float* lse_acc, const float* o_part,
                                                     const float* lse_part, uint16_t* out, int64_t rows,
@@ -511,6 +524,33 @@ __global__ void __launch_bounds__(256) merge_kernel(float* o_acc, float* lse_acc
   }
 }
 
+// ---- staging copy of one ring step's K and V blocks (the stand-in for the
+// peer-to-peer receive), run on the copy stream beside a step kernel ----
+// One wave per SIMD and at most 16 VGPRs, so that it fits next to the 8-wave
+// step workgroup (248 VGPRs per wave) on every CU; the waves raise their
+// issue priority because they mostly wait on memory, and without it the
+// older step waves would starve them.  K is copied first, then V, in 16-byte
+// chunks; every lane keeps two chunks in flight.
+__device__ __forceinline__ void copy_range(const u32x4* __restrict__ src, u32x4* __restrict__ dst, unsigned n,
+                                           unsigned i, unsigned stride) {
+  for (; i + stride < n; i += 2 * stride) {
+    const u32x4 x = src[i];
+    const u32x4 y = src[i + stride];
+    dst[i] = x;
+    dst[i + stride] = y;
+  }
+  if (i < n) dst[i] = src[i];
+}
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(8)))
+    stage_copy_kernel(const u32x4* __restrict__ k_src, u32x4* __restrict__ k_dst, const u32x4* __restrict__ v_src,
+                      u32x4* __restrict__ v_dst, unsigned n16) {
+  __builtin_amdgcn_s_setprio(3);
+  const unsigned stride = gridDim.x * blockDim.x;
+  const unsigned i = blockIdx.x * blockDim.x + threadIdx.x;
+  copy_range(k_src, k_dst, n16, i, stride);
+  copy_range(v_src, v_dst, n16, i, stride);
+}
+
 }  // namespace
 
 int step_block_rows(int q_chunk_len) {
@@ -523,14 +563,26 @@ hipError_t launch_step(const StepArgs& a, int D, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk((unsigned)(2 * bm));  // one wave per 32 rows
   if (D == 128) {
-    if (bm == 256) hipLaunchKernelGGL((step_kernel<128, 8>), g, blk, 0, stream, a);
-    else if (bm == 128) hipLaunchKernelGGL((step_kernel<128, 4>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((step_kernel<128, 2>), g, blk, 0, stream, a);
+    if (bm == 256) hipLaunchKernelGGL((step_kernel_256<128>), g, blk, 0, stream, a);
+    else if (bm == 128) hipLaunchKernelGGL((step_kernel_small<128, 4>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((step_kernel_small<128, 2>), g, blk, 0, stream, a);
   } else {
-    if (bm == 256) hipLaunchKernelGGL((step_kernel<64, 8>), g, blk, 0, stream, a);
-    else if (bm == 128) hipLaunchKernelGGL((step_kernel<64, 4>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((step_kernel<64, 2>), g, blk, 0, stream, a);
+    if (bm == 256) hipLaunchKernelGGL((step_kernel_256<64>), g, blk, 0, stream, a);
+    else if (bm == 128) hipLaunchKernelGGL((step_kernel_small<64, 4>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((step_kernel_small<64, 2>), g, blk, 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_copy(const void* k_src, void* k_dst, const void* v_src, void* v_dst, size_t bytes,
+                             hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  if (bytes % 16 != 0 || bytes / 16 > 0x7fffffffull) return hipErrorInvalidValue;
+  const unsigned n16 = (unsigned)(bytes / 16);
+  unsigned blocks = (n16 + 255) / 256;
+  if (blocks > 256) blocks = 256;  // one workgroup per CU
+  hipLaunchKernelGGL(stage_copy_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const u32x4*>(k_src),
+                     static_cast<u32x4*>(k_dst), static_cast<const u32x4*>(v_src), static_cast<u32x4*>(v_dst), n16);
   return hipGetLastError();
 }
 
