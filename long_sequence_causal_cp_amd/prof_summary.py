@@ -87,12 +87,49 @@ def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, ke
     }
 
 
+SQ_NAMES = ["SQ_WAVES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES",
+            "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def sq_text(pmc_csv: str, cmd: str, kernel: str = "step_kernel", n_xcd: int = 8, n_simd: int = 1024) -> str:
+    """Per-dispatch means of the SQ counters and the MFMA-busy fraction.
+
+    GRBM_GUI_ACTIVE is summed over the XCDs, so cycles per XCD = value / n_xcd;
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles per XCD * n_simd).
+    """
+    agg = {}
+    for r in _rows(pmc_csv):
+        if kernel in r["Kernel_Name"]:
+            agg.setdefault(int(r["Grid_Size"]), {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = [f"command: {cmd}", f"kernel: every dispatch whose name contains '{kernel}'; mean per dispatch", ""]
+    for grid, counters in sorted(agg.items()):
+        out.append(f"grid {grid} threads:")
+        vals = {n: statistics.fmean(counters[n]) for n in SQ_NAMES if n in counters}
+        for n in SQ_NAMES:
+            if n in vals:
+                out.append(f"  {n:28s} {vals[n]:16.1f}   ({len(counters[n])} dispatches)")
+        if "GRBM_GUI_ACTIVE" in vals and "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+            per_xcd = vals["GRBM_GUI_ACTIVE"] / n_xcd
+            out.append(f"  derived: cycles per XCD {per_xcd:.0f}; MFMA busy "
+                       f"{100 * vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (per_xcd * n_simd):.1f} %")
+        if "SQ_WAVES" in vals and vals["SQ_WAVES"] > 0:
+            w = vals["SQ_WAVES"]
+            out.append(f"  derived: per wave {vals.get('SQ_INSTS_MFMA', 0) / w:.0f} MFMA, "
+                       f"{vals.get('SQ_INSTS_VALU', 0) / w:.0f} VALU (incl. MFMA), "
+                       f"{vals.get('SQ_INSTS_LDS', 0) / w:.0f} LDS instructions")
+        out.append("")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="sub", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--cmd", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("csv")
+    q.add_argument("--cmd", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -105,6 +142,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.sub == "stats":
         sys.stdout.write(stats_text(a.csv, a.cmd))
+        return
+    if a.sub == "sq":
+        sys.stdout.write(sq_text(a.csv, a.cmd))
         return
     res = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes)
     res.update({"workload": a.workload, "kernel_source_sha256": kernel_source_sha256(), "commands": a.commands})
