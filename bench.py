@@ -203,9 +203,12 @@ def main():
     ms_per_step_instrumented = ek0.elapsed_time(ek1) / args.steps
 
     n_launch = len(kern_ms)
-    assert n_launch == args.steps * N, (n_launch, args.steps * N)
+    assert n_launch > 0 and n_launch % args.steps == 0, (n_launch, args.steps)
+    launches_per_step = n_launch // args.steps  # step-kernel launches per ring forward
     avg_kernel_ms = statistics.fmean(kern_ms)
-    per_launch_flops = flops / N
+    # a ring forward's algorithmic flops spread over its launches (the launches
+    # differ in size: step 0 alone, later steps two per launch)
+    per_launch_flops = flops / launches_per_step
     achieved = per_launch_flops / (avg_kernel_ms * 1e-3) / 1e12
     # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counters, only if they
     # were taken on this workload and on the kernel source that is built now
@@ -266,6 +269,8 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "launches": n_launch,
+            "launches_per_step": launches_per_step,
+            "flop_per_launch": per_launch_flops,
             "avg_launch_ms": round(avg_kernel_ms, 5),
             "ms_per_step_with_kernel_events": round(ms_per_step_instrumented, 5),
         },

@@ -132,9 +132,10 @@ cp_status_t cp_attn_merge(float* o_acc, float* lse_acc,
                           int B, int H, int Sq, int D, void* out_bf16_or_null,
                           hipStream_t stream);
 
-/* Workspace bytes cp_ring_attn_fwd needs: two staging slots for one K and one
- * V block [B,H,Skv,D] bf16, plus the fp32 running output [B,H,Sq,D],
- * each rounded up to 256 bytes.  Returns 0 for non-positive sizes. */
+/* Workspace bytes cp_ring_attn_fwd needs: two staging slots, each for the K
+ * and V blocks [B,H,Skv,D] bf16 of two ring steps (eight blocks), plus the
+ * fp32 running output [B,H,Sq,D], each rounded up to 256 bytes.  Returns 0
+ * for non-positive sizes. */
 size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq);
 
 /*
@@ -148,12 +149,18 @@ size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq);
  *             workspace on copy_stream, standing in for the peer-to-peer
  *             receive ([MLM] section 5: double buffering on a separate
  *             stream; [RAF] section 3: receive from the previous rank).
+ *             After step 0, steps are computed two per kernel launch (one
+ *             when a single step is left, or when a step has more than
+ *             CP_MAX_CHUNKS / 2 chunks): a slot holds the blocks of the two
+ *             steps of one launch, and the online softmax runs on across the
+ *             two blocks, which equals merging the two steps' partial results
+ *             by their log-sum-exp.
  *   out       bf16 [B,H,Sq,D], lse fp32 [B,H,Sq]  (final results)
  *   workspace at least cp_ring_attn_workspace_bytes(B,H,Skv,D,Sq) bytes,
  *             256-byte aligned.
  *   copy_stream  a stream other than `stream` (not NULL).
- * The copy of step j+1 overlaps the compute of step j; the copy into a slot
- * waits until the step that last read that slot has finished.  On entry
+ * The copies for launch g+1 overlap the compute of launch g; the copy into a
+ * slot waits until the launch that last read that slot has finished.  On entry
  * copy_stream waits for prior work on `stream`; before returning, `stream`
  * waits for every copy, so later work on `stream` is ordered after the call.
  * Every query row must see at least one key over the steps (true for a

@@ -98,24 +98,33 @@ long long pairs_for_chunk(const cp_chunks_t* q, int c, const cp_chunks_t* kv) {
   return p;
 }
 
-// Fill the launch arguments shared by every step; flags/order set by caller.
+// Append the chunks of one [BH, Skv, D] K/V block (table `kvc`) to a launch.
+void add_kv_block(StepArgs& a, const void* k, const void* v, const cp_chunks_t* kvc) {
+  for (int i = 0; i < kvc->n_chunks; ++i, ++a.n_kv_chunks) {
+    const size_t off = (size_t)i * kvc->chunk_len * (size_t)a.D;
+    a.kc[a.n_kv_chunks] = static_cast<const uint16_t*>(k) + off;
+    a.vc[a.n_kv_chunks] = static_cast<const uint16_t*>(v) + off;
+    a.kv_start[a.n_kv_chunks] = (int)kvc->start[i];
+  }
+}
+
+// Fill the launch arguments shared by every step for one K/V block; flags
+// and order are set by the caller, further blocks added by add_kv_block.
 void base_args(StepArgs& a, const void* q, const void* k, const void* v, float* o, float* lse, void* out,
-               int B, int H, const cp_chunks_t* qc, const cp_chunks_t* kvc, float scale) {
+               int B, int H, int D, const cp_chunks_t* qc, const cp_chunks_t* kvc, float scale) {
   std::memset(&a, 0, sizeof(a));
   a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
   a.o_run = o;
   a.lse_run = lse;
   a.out = static_cast<uint16_t*>(out);
   a.BH = B * H;
+  a.D = D;
   a.Sq = qc->n_chunks * qc->chunk_len;
   a.Skv = kvc->n_chunks * kvc->chunk_len;
   a.q_chunk_len = qc->chunk_len;
   a.kv_chunk_len = kvc->chunk_len;
-  a.n_kv_chunks = kvc->n_chunks;
   for (int i = 0; i < qc->n_chunks; ++i) a.q_start[i] = (int)qc->start[i];
-  for (int i = 0; i < kvc->n_chunks; ++i) a.kv_start[i] = (int)kvc->start[i];
+  add_kv_block(a, k, v, kvc);
   a.rb_per_chunk = qc->chunk_len / cpattn::step_block_rows(qc->chunk_len);
   a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -244,7 +253,7 @@ cp_status_t cp_attn_step_fwd(const void* q, const void* k, const void* v, float*
     return fail(CP_ERR_INVALID, "o, lse and out must not overlap");
 
   StepArgs a;
-  base_args(a, q, k, v, o, lse, out_bf16_or_null, B, H, q_chunks, kv_chunks, softmax_scale);
+  base_args(a, q, k, v, o, lse, out_bf16_or_null, B, H, D, q_chunks, kv_chunks, softmax_scale);
   std::vector<int> active;
   std::vector<long long> work(CP_MAX_CHUNKS, 0);
   for (int c = 0; c < q_chunks->n_chunks; ++c) {
@@ -287,7 +296,7 @@ size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq) {
   if (B <= 0 || H <= 0 || Skv <= 0 || D <= 0 || Sq <= 0) return 0;
   const size_t kv = round256((size_t)B * H * Skv * D * 2);
   const size_t o = round256((size_t)B * H * Sq * D * 4);
-  return 4 * kv + o;
+  return 8 * kv + o;
 }
 
 cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const void* const* k_steps,
@@ -336,32 +345,50 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
         return fail(CP_ERR_INVALID, "out, lse and workspace must not overlap");
   }
 
-  // ---- plan: which query chunks work at which step, and how ----
+  // ---- plan ----
+  // Launches: step 0 on the caller's block, then the later steps two at a
+  // time (one launch attends the query block to both staged blocks; a single
+  // step when one is left over or when two steps' chunks exceed the launch's
+  // chunk table).  Staging is double buffered per launch: the blocks of
+  // launch g go to pair slot g % 2 on copy_stream while launch g-1 computes.
+  const int nkv = kv_chunks_steps[0].n_chunks;
+  const int per = (2 * nkv <= CP_MAX_CHUNKS) ? 2 : 1;  // ring steps per staged launch
+  std::vector<int> l_first, l_count;                   // launches: first step, number of steps
+  l_first.push_back(0);
+  l_count.push_back(1);
+  for (int j = 1; j < n_steps; j += per) {
+    l_first.push_back(j);
+    l_count.push_back(std::min(per, n_steps - j));
+  }
+  const int n_launch = (int)l_first.size();
   const int nq = q_chunks->n_chunks;
-  std::vector<std::vector<long long>> work(n_steps, std::vector<long long>(CP_MAX_CHUNKS, 0));
+  std::vector<std::vector<long long>> work(n_launch, std::vector<long long>(CP_MAX_CHUNKS, 0));
   std::vector<int> first(nq, -1), last(nq, -1);
-  for (int j = 0; j < n_steps; ++j)
+  for (int l = 0; l < n_launch; ++l)
     for (int c = 0; c < nq; ++c) {
-      work[j][c] = pairs_for_chunk(q_chunks, c, &kv_chunks_steps[j]);
-      if (work[j][c] > 0) {
-        if (first[c] < 0) first[c] = j;
-        last[c] = j;
+      for (int j = l_first[l]; j < l_first[l] + l_count[l]; ++j)
+        work[l][c] += pairs_for_chunk(q_chunks, c, &kv_chunks_steps[j]);
+      if (work[l][c] > 0) {
+        if (first[c] < 0) first[c] = l;
+        last[c] = l;
       }
     }
   for (int c = 0; c < nq; ++c)
-    if (first[c] < 0) first[c] = last[c] = n_steps - 1;  // no key at all: write O = 0, LSE = -inf
+    if (first[c] < 0) first[c] = last[c] = n_launch - 1;  // no key at all: write O = 0, LSE = -inf
 
+  // workspace: K pair slots [0,2) and [2,4), V pair slots [4,6) and [6,8) (in
+  // blocks of kv_slot bytes), then the fp32 running O
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const size_t kv_slot = round256(kv_bytes);
-  void* slot_k[2] = {ws, ws + 2 * kv_slot};
-  void* slot_v[2] = {ws + kv_slot, ws + 3 * kv_slot};
-  float* o_run = reinterpret_cast<float*>(ws + 4 * kv_slot);
+  auto slot_k = [&](int g, int i) -> void* { return ws + (size_t)(2 * (g & 1) + i) * kv_slot; };
+  auto slot_v = [&](int g, int i) -> void* { return ws + (size_t)(4 + 2 * (g & 1) + i) * kv_slot; };
+  float* o_run = reinterpret_cast<float*>(ws + 8 * kv_slot);
 
   std::vector<hipEvent_t> ev;
-  if ((st = get_events(2 + 2 * n_steps, ev)) != CP_OK) return st;
+  if ((st = get_events(2 + 2 * n_launch, ev)) != CP_OK) return st;
   hipEvent_t ev_entry = ev[0], ev_done = ev[1];
-  hipEvent_t* copied = &ev[2];
-  hipEvent_t* released = &ev[2 + n_steps];
+  hipEvent_t* copied = &ev[2];              // per launch: its blocks are staged
+  hipEvent_t* released = &ev[2 + n_launch];  // per launch: done reading its slot
 
   hipError_t e;
 #define HIP_TRY(call, what)                 \
@@ -369,35 +396,50 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
     if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
   } while (0)
 
-  auto stage = [&](int j) -> cp_status_t {  // copy step j's block into slot j%2 on copy_stream
-    if (j >= 3) HIP_TRY(hipStreamWaitEvent(copy_stream, released[j - 2], 0), "hipStreamWaitEvent");
-    HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k[j & 1], v_steps[j], slot_v[j & 1], kv_bytes, copy_stream),
-            "staging copy launch");
-    HIP_TRY(hipEventRecord(copied[j], copy_stream), "hipEventRecord");
+  // copy the blocks of staged launch l (>= 1, pair slot g = l - 1) on copy_stream
+  auto stage = [&](int l) -> cp_status_t {
+    const int g = l - 1;
+    if (g >= 2) HIP_TRY(hipStreamWaitEvent(copy_stream, released[l - 2], 0), "hipStreamWaitEvent");
+    for (int i = 0; i < l_count[l]; ++i) {
+      const int j = l_first[l] + i;
+      HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k(g, i), v_steps[j], slot_v(g, i), kv_bytes, copy_stream),
+              "staging copy launch");
+    }
+    HIP_TRY(hipEventRecord(copied[l], copy_stream), "hipEventRecord");
     return CP_OK;
   };
 
   HIP_TRY(hipEventRecord(ev_entry, stream), "hipEventRecord");
   HIP_TRY(hipStreamWaitEvent(copy_stream, ev_entry, 0), "hipStreamWaitEvent");
-  if (n_steps > 1 && (st = stage(1)) != CP_OK) return st;
-  for (int j = 0; j < n_steps; ++j) {
-    // the copy for step j+1 goes into the slot step j-1 read; it overlaps step j
-    if (j + 1 >= 2 && j + 1 < n_steps && (st = stage(j + 1)) != CP_OK) return st;
-    if (j >= 1) HIP_TRY(hipStreamWaitEvent(stream, copied[j], 0), "hipStreamWaitEvent");
-    const void* kj = (j == 0) ? k_steps[0] : slot_k[j & 1];
-    const void* vj = (j == 0) ? v_steps[0] : slot_v[j & 1];
+  for (int l = 1; l < n_launch && l <= 2; ++l)
+    if ((st = stage(l)) != CP_OK) return st;
+  for (int l = 0; l < n_launch; ++l) {
+    if (l >= 1) HIP_TRY(hipStreamWaitEvent(stream, copied[l], 0), "hipStreamWaitEvent");
     StepArgs a;
-    base_args(a, q, kj, vj, o_run, lse, out, B, H, q_chunks, &kv_chunks_steps[j], softmax_scale);
+    const int j0 = l_first[l];
+    if (l == 0) {
+      base_args(a, q, k_steps[0], v_steps[0], o_run, lse, out, B, H, D, q_chunks, &kv_chunks_steps[0],
+                softmax_scale);
+    } else {
+      base_args(a, q, slot_k(l - 1, 0), slot_v(l - 1, 0), o_run, lse, out, B, H, D, q_chunks,
+                &kv_chunks_steps[j0], softmax_scale);
+      for (int i = 1; i < l_count[l]; ++i)
+        add_kv_block(a, slot_k(l - 1, i), slot_v(l - 1, i), &kv_chunks_steps[j0 + i]);
+    }
     std::vector<int> active;
     for (int c = 0; c < nq; ++c) {
-      if (j < first[c] || j > last[c] || (work[j][c] == 0 && j != last[c] && j != first[c])) continue;
+      if (l < first[c] || l > last[c] || (work[l][c] == 0 && l != last[c] && l != first[c])) continue;
       active.push_back(c);
-      a.flags[c] = (j == first[c] ? 0 : cpattn::kFlagMerge) |
-                   (j == last[c] ? cpattn::kFlagFinalize : cpattn::kFlagWriteO);
+      a.flags[c] = (l == first[c] ? 0 : cpattn::kFlagMerge) |
+                   (l == last[c] ? cpattn::kFlagFinalize : cpattn::kFlagWriteO) | cpattn::kFlagLaneO;
     }
-    set_order(a, active, work[j]);
+    set_order(a, active, work[l]);
     HIP_TRY(launch_step_timed(a, D, stream), "step kernel launch");
-    if (j + 2 < n_steps) HIP_TRY(hipEventRecord(released[j], stream), "hipEventRecord");
+    if (l + 2 < n_launch) {
+      // launch l + 2 reuses the pair slot launch l reads
+      if (l >= 1) HIP_TRY(hipEventRecord(released[l], stream), "hipEventRecord");
+      if (l + 2 >= 3 && (st = stage(l + 2)) != CP_OK) return st;
+    }
   }
   HIP_TRY(hipEventRecord(ev_done, copy_stream), "hipEventRecord");
   HIP_TRY(hipStreamWaitEvent(stream, ev_done, 0), "hipStreamWaitEvent");

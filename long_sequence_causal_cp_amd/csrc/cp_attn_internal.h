@@ -15,20 +15,24 @@ enum : int {
   kFlagMerge = 1,     // read the running (O, LSE) and merge; else overwrite
   kFlagFinalize = 2,  // write bf16 output
   kFlagWriteO = 4,    // write the fp32 running O
+  kFlagLaneO = 8,     // the running O is kept in the step kernel's lane order (see the kernel)
 };
 
 // Everything one launch of the step kernel needs; passed by value.
 struct StepArgs {
   const uint16_t* q;  // bf16 [BH, Sq, D]
-  const uint16_t* k;  // bf16 [BH, Skv, D]
-  const uint16_t* v;  // bf16 [BH, Skv, D]
+  // K/V chunk c: its first row for (b, h) = 0; (b, h) adds bh * Skv * D.  The
+  // chunks of one launch may come from different [BH, Skv, D] blocks (one
+  // launch can cover two ring steps), so each has its own base.
+  const uint16_t* kc[kMaxChunks];
+  const uint16_t* vc[kMaxChunks];
   float* o_run;       // fp32 [BH, Sq, D] (may be null when no chunk has kFlagWriteO/kFlagMerge)
   float* lse_run;     // fp32 [BH, Sq]
   uint16_t* out;      // bf16 [BH, Sq, D] (may be null when no chunk finalizes)
-  int BH;
-  int Sq, Skv;
+  int BH, D;
+  int Sq, Skv;                // rows per (b, h) of the query block and of every K/V block
   int q_chunk_len, kv_chunk_len;
-  int n_kv_chunks;
+  int n_kv_chunks;            // chunks of this launch, visited in index order
   int n_order;                // active query chunks in this launch
   int order[kMaxChunks];      // their indices, heaviest first
   int flags[kMaxChunks];      // per query chunk index

@@ -11,14 +11,17 @@
 //
 // Step kernel.  One workgroup owns BM = 32*NW consecutive query rows of one
 // (batch, head) inside one query chunk; each wave owns 32 of them.  K and V
-// tiles of 64 keys are staged HBM -> registers -> LDS (16-byte loads, double
-// buffered, one barrier per tile).  Per tile a wave computes the transposed
-// score block S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that every lane
-// holds one query's scores; the causal mask, the row maximum and the
-// exponentials are then lane-local, with one cross-half exchange
-// (v_permlane32_swap) per tile.  P^T feeds the second MFMA directly from
-// registers; V^T comes from the row-major V tile through the gfx950 LDS
-// transpose read (ds_read_b64_tr_b16).  The epilogue divides by the row sum,
+// tiles of 64 keys are staged HBM -> LDS by direct-to-LDS 16-byte loads,
+// double buffered, one barrier per tile.  Per 32-key sub-tile a wave computes
+// the transposed score block S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so
+// that every lane holds one query's scores; the causal mask and the
+// exponentials are then lane-local.  The exponentials are taken against the
+// running maximum as it stands; only when a lane's sum shows that some
+// probability outgrew the lazy-rescale bound (and on a row's first
+// sub-tile) is the row maximum formed (one v_permlane32_swap across the two
+// halves of the row) and the sub-tile redone.  P^T feeds the second MFMA
+// directly from registers; V^T comes from the row-major V tile through the
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  The epilogue normalises,
 // forms the natural-log LSE and merges into the running fp32 result by
 // log-sum-exp rescaling, optionally writing the bf16 output.
 #include "cp_attn_internal.h"
@@ -32,6 +35,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -44,6 +48,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 // A row's stored maximum is only raised when a tile exceeds it by more than
 // 2^8 in probability scale; smaller excesses leave p <= 256, exact in fp32.
 constexpr float kRescaleThreshold = 8.0f;
+// A lane's 16 exponentials of a sub-tile against an unchanged maximum are
+// accepted while their sum stays at or below 16 * 2^kRescaleThreshold (so
+// every accepted p is at most 2^12); a larger sum means some p above
+// 2^kRescaleThreshold, i.e. a row maximum that the lazy update raises.
+constexpr float kSumLimit = 4096.0f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -118,12 +127,11 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Four-wave workgroups are built for two waves per SIMD (at most 256 VGPRs),
-// so two workgroups share a CU.  Each wave runs a software pipeline over
-// 32-key sub-tiles u (two per 64-key LDS tile): sub-iteration u computes the
-// exponentials of sub-tile u while its MFMAs are QK^T of sub-tile u+1 and PV
-// of sub-tile u-1, neither of which depends on that sub-iteration's VALU
-// work, so the two streams interleave freely.
+// Each wave runs a software pipeline over 32-key sub-tiles u (two per
+// 64-key LDS tile): sub-iteration u computes the exponentials of sub-tile u
+// while its MFMAs are QK^T of sub-tile u+1 and PV of sub-tile u-1, neither of
+// which depends on that sub-iteration's VALU work, so the two streams
+// interleave freely.
 template <int D, int NW>
 __device__ __forceinline__ void step_body(const StepArgs& a) {
   constexpr int BM = 32 * NW;
@@ -191,29 +199,28 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) kv_start[c] = a.kv_start[c];
   struct Cursor {
-    int c, left, krow, kpos;
+    int c, left, kpos;
+    const uint16_t* kp;  // the tile's first K row
+    const uint16_t* vp;  // and V row
   };
   // first visible tile of a chunk after chunk `after` (c = kMaxChunks if none)
   auto chunk_after = [&](int after) {
-    Cursor t{kMaxChunks, 0, 0, 0};
+    Cursor t{kMaxChunks, 0, 0, a.kc[0], a.vc[0]};
 #pragma unroll
     for (int c = kMaxChunks - 1; c >= 0; --c)
-      if (c > after && n_vis[c] > 0) t = Cursor{c, n_vis[c], c * a.kv_chunk_len, kv_start[c]};
+      if (c > after && n_vis[c] > 0) t = Cursor{c, n_vis[c], kv_start[c], a.kc[c] + bh_kv * D, a.vc[c] + bh_kv * D};
     return t;
   };
   auto next_tile = [&](Cursor t) {
     t.left -= 1;
-    t.krow += kTileKeys;
     t.kpos += kTileKeys;
+    t.kp += kTileKeys * D;
+    t.vp += kTileKeys * D;
     if (t.left <= 0) t = chunk_after(t.c);  // rare: chunk boundary
     return t;
   };
-  auto load_k = [&](const Cursor& t, unsigned char* buf) {
-    tile_to_lds<D, NW, true>(a.k + (bh_kv + t.krow) * D, buf, wave_u, lane);
-  };
-  auto load_v = [&](const Cursor& t, unsigned char* buf) {
-    tile_to_lds<D, NW, false>(a.v + (bh_kv + t.krow) * D, buf, wave_u, lane);
-  };
+  auto load_k = [&](const Cursor& t, unsigned char* buf) { tile_to_lds<D, NW, true>(t.kp, buf, wave_u, lane); };
+  auto load_v = [&](const Cursor& t, unsigned char* buf) { tile_to_lds<D, NW, false>(t.vp, buf, wave_u, lane); };
 
   // Q^T fragments: lane holds Q[row lq][16s + 8g .. +8]
   bf16x8 qf[NS];
@@ -227,7 +234,8 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   float m_run = neg_inf();  // running max, log2-scaled units
-  float l_lane = 0.f;       // this lane's share of the row sum
+  float l_lane = 0.f;       // this lane's share of the row sum (fp32 exponentials)
+  float r_lane = 0.f;       // the same over the bf16-rounded exponentials
 
   // per-lane constant parts of the LDS reads
   const int k_base = k_lds_off(lq, 0, g);
@@ -252,15 +260,44 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     return s;
   };
 
+  // Exponentials of one sub-tile against the shift `negm` (minus the row's
+  // reference maximum): P(u) in bf16 and two sums of this lane's share of the
+  // row: `lsum` of the fp32 values (for the log-sum-exp) and `rsum` of the
+  // rounded bf16 values that the PV product consumes (the normaliser of the
+  // output, so that its weights sum to one exactly as applied).
+  auto exps = [&](const f32x16& s_cur, bf16x8 (&p_cur)[2], float negm, float& rsum) {
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float lsum = 0.f;
+    rsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[8 * t + e], a.scale_log2, negm));
+        lsum += p;
+        p_cur[t][e] = (__bf16)p;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 pr = {p_cur[t][2 * j], p_cur[t][2 * j + 1]};
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rsum, false);
+      }
+    }
+    return lsum;
+  };
+
   // The branch-free body of sub-iteration u.
-  //   exp:  row max of s_cur (scores of sub-tile u) -> lazy max update -> 16
-  //         exponentials per lane, their row sum and bf16 packing into p_cur;
+  //   exp:  16 exponentials per lane of s_cur (scores of sub-tile u) against
+  //         the running maximum as it stands, packed to bf16 into p_cur, and
+  //         their row sum (returned in lsum);
   //   QK:   s_nxt = K Q^T of sub-tile u+1, rows [32 hn, +32) of `kn` (kQK);
   //   PV:   O^T += V^T P^T of sub-tile u-1, rows [32 hp, +32) of `vp` (kPV).
-  // Returns the factor the output must be scaled by once PV(u-1) is in.
+  // Returns true in a lane whose exponentials must be redone with a new
+  // maximum: its sum exceeds kSumLimit, so some p exceeds 2^kRescaleThreshold
+  // (inf or NaN while the row has no maximum yet, m_run = -inf).
   auto body = [&](const f32x16& s_cur, f32x16& s_nxt, bf16x8 (&p_cur)[2], const bf16x8 (&p_prev)[2],
-                  const unsigned char* kn, int hn, const unsigned char* vp, int hp, auto exp_tag, auto qk_tag,
-                  auto pv_tag) {
+                  const unsigned char* kn, int hn, const unsigned char* vp, int hp, float& lsum, float& rsum, auto exp_tag,
+                  auto qk_tag, auto pv_tag) {
     constexpr bool kExp = decltype(exp_tag)::value;
     constexpr bool kQK = decltype(qk_tag)::value;
     constexpr bool kPV = decltype(pv_tag)::value;
@@ -284,26 +321,10 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
         }
       }
     }
-    if constexpr (!kExp) return 1.f;
-    // VALU stream
-    float mx = neg_inf();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
-    mx = xhalf_max(mx) * a.scale_log2;
-    const float m_new = (mx > m_run + kRescaleThreshold) ? mx : m_run;
-    const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    const float negm = (m_run == neg_inf()) ? 0.f : -m_run;
-    float lsum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[8 * t + e], a.scale_log2, negm));
-        lsum += p;
-        p_cur[t][e] = (__bf16)p;
-      }
-    l_lane = __builtin_fmaf(l_lane, alpha, lsum);
+    if constexpr (!kExp) return false;
+    // VALU stream.  -m_run is +inf while the row has no maximum: every p is
+    // then inf (or NaN where masked) and the test below fails.
+    lsum = exps(s_cur, p_cur, -m_run, rsum);
     // interleave: each MFMA followed by its share of LDS reads and VALU work
     constexpr int kMfma = (kQK ? NS : 0) + (kPV ? 2 * NDB : 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -311,9 +332,9 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     for (int i = 0; i < kMfma; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-    return alpha;
+    return !(lsum <= kSumLimit);
   };
 
   auto mask = [&](f32x16& s, int kpos) {
@@ -325,20 +346,40 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     }
   };
   // Sub-iteration u: mask S(u) (first key at kpos) if it crosses this wave's
-  // diagonal, run the body, then (rarely) rescale the output once PV(u-1)
-  // is in.
+  // diagonal and run the body.  Rarely (once at the start, and when the
+  // scores outgrow the running maximum) the exponentials are redone: the
+  // lazy maximum update raises a row's maximum only when the sub-tile's
+  // exceeds it by more than kRescaleThreshold, and the output, with PV(u-1)
+  // in, is rescaled to the new maximum.
   auto sub = [&](int kpos, f32x16& s_cur, f32x16& s_nxt, bf16x8 (&p_cur)[2], const bf16x8 (&p_prev)[2],
                  const unsigned char* kn, int hn, const unsigned char* vp, int hp, auto exp_tag, auto qk_tag,
                  auto pv_tag) {
-    if constexpr (decltype(exp_tag)::value) {
+    constexpr bool kExp = decltype(exp_tag)::value;
+    if constexpr (kExp) {
       if (kpos + 31 > qw_pos) mask(s_cur, kpos);
     }
-    const float alpha = body(s_cur, s_nxt, p_cur, p_prev, kn, hn, vp, hp, exp_tag, qk_tag, pv_tag);
-    if (__any(alpha != 1.f)) {  // rare: the running max moved; P(u) is on the new scale
+    float lsum = 0.f, rsum = 0.f;
+    const bool redo = body(s_cur, s_nxt, p_cur, p_prev, kn, hn, vp, hp, lsum, rsum, exp_tag, qk_tag, pv_tag);
+    if constexpr (kExp) {
+      float alpha = 1.f;
+      if (__any(redo)) {
+        float mx = neg_inf();
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+        mx = xhalf_max(mx) * a.scale_log2;
+        const float m_new = (mx > m_run + kRescaleThreshold) ? mx : m_run;
+        alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        lsum = exps(s_cur, p_cur, (m_run == neg_inf()) ? 0.f : -m_run, rsum);
+        if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+      }
+      l_lane = __builtin_fmaf(l_lane, alpha, lsum);
+      r_lane = __builtin_fmaf(r_lane, alpha, rsum);
     }
   };
   // Cursors at pair n: tm = tile n, tv = tile n+1, tk = tile n+2.
@@ -405,9 +446,12 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   }
 
   // ---- epilogue: normalise, LSE, merge, write ----
+  // LSE from the fp32 row sum; the output is normalised by the sum of the
+  // bf16 weights it was accumulated with
   const float l = xhalf_sum(l_lane);
+  const float r = xhalf_sum(r_lane);
   const float lse_j = (l > 0.f) ? (m_run + __log2f(l)) * kLn2 : neg_inf();
-  const float inv_l = (l > 0.f) ? 1.f / l : 0.f;
+  const float inv_l = (l > 0.f && r > 0.f) ? 1.f / r : 0.f;
   const size_t row = bh_q + qw_local + lq;
   float w_prev = 0.f, w_cur = inv_l, lse_new = lse_j;
   if (flags & kFlagMerge) {
@@ -430,21 +474,32 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   if (g == 0) a.lse_run[row] = lse_new;
   const bool write_o = (flags & kFlagWriteO) != 0;
   const bool finalize = (flags & kFlagFinalize) != 0;
+  // The running O of this wave's 32 rows occupies the 32 x D floats at
+  // o_run + (bh_q + qw_local) D.  In row-major order a lane's 16-byte piece
+  // (d0 .. d0+3 of row lq) lands 32 rows apart from its neighbours' pieces;
+  // in lane order (kFlagLaneO, the ring driver's private workspace) piece k
+  // of lane L is the 16 bytes at float (64 k + L) 4 of the block, so each
+  // wave load or store covers one contiguous KiB.
+  // Either way piece k = 4 db + rr sits at o_base + k * o_stride.
+  const bool lane_order = (flags & kFlagLaneO) != 0;
+  float* const o_base = a.o_run + (bh_q + qw_local) * D + (lane_order ? lane * 4 : lq * D + 4 * g);
+  const int o_stride = lane_order ? 256 : 8;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int d0 = 32 * db + 8 * rr + 4 * g;
+      float* const o_ptr = o_base + (4 * db + rr) * o_stride;
       f32x4 o;
       o[0] = oacc[db][4 * rr + 0] * w_cur;
       o[1] = oacc[db][4 * rr + 1] * w_cur;
       o[2] = oacc[db][4 * rr + 2] * w_cur;
       o[3] = oacc[db][4 * rr + 3] * w_cur;
       if (w_prev != 0.f) {
-        const f32x4 prev = *reinterpret_cast<const f32x4*>(a.o_run + row * D + d0);
+        const f32x4 prev = *reinterpret_cast<const f32x4*>(o_ptr);
         o += w_prev * prev;
       }
-      if (write_o) *reinterpret_cast<f32x4*>(a.o_run + row * D + d0) = o;
+      if (write_o) *reinterpret_cast<f32x4*>(o_ptr) = o;
       if (finalize) {
         bf16x4 h;
         h[0] = (__bf16)o[0];
