@@ -35,7 +35,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -45,14 +44,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// A row's stored maximum is only raised when a tile exceeds it by more than
-// 2^8 in probability scale; smaller excesses leave p <= 256, exact in fp32.
-constexpr float kRescaleThreshold = 8.0f;
-// A lane's 16 exponentials of a sub-tile against an unchanged maximum are
-// accepted while their sum stays at or below 16 * 2^kRescaleThreshold (so
-// every accepted p is at most 2^12); a larger sum means some p above
-// 2^kRescaleThreshold, i.e. a row maximum that the lazy update raises.
-constexpr float kSumLimit = 4096.0f;
+// Lazy rescaling.  A lane's 16 exponentials of a sub-tile, taken against the
+// row maximum as it stands, are accepted while their sum is at most
+// kSumLimit, so every accepted p is at most 2^8 (exact headroom in fp32, and
+// the same relative rounding in bf16).  A larger sum (inf or NaN while a row
+// has no maximum yet) sends the wave to the slow path, which raises each
+// row's maximum to the sub-tile's, rescales the output and redoes the
+// sub-tile.
+constexpr float kSumLimit = 256.0f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -234,8 +233,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   float m_run = neg_inf();  // running max, log2-scaled units
-  float l_lane = 0.f;       // this lane's share of the row sum (fp32 exponentials)
-  float r_lane = 0.f;       // the same over the bf16-rounded exponentials
+  float l_lane = 0.f;       // this lane's share of the row sum
 
   // per-lane constant parts of the LDS reads
   const int k_base = k_lds_off(lq, 0, g);
@@ -261,28 +259,18 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   };
 
   // Exponentials of one sub-tile against the shift `negm` (minus the row's
-  // reference maximum): P(u) in bf16 and two sums of this lane's share of the
-  // row: `lsum` of the fp32 values (for the log-sum-exp) and `rsum` of the
-  // rounded bf16 values that the PV product consumes (the normaliser of the
-  // output, so that its weights sum to one exactly as applied).
-  auto exps = [&](const f32x16& s_cur, bf16x8 (&p_cur)[2], float negm, float& rsum) {
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  // reference maximum): P(u) in bf16 and this lane's share of its row sum,
+  // summed in fp32 before rounding.
+  auto exps = [&](const f32x16& s_cur, bf16x8 (&p_cur)[2], float negm) {
     float lsum = 0.f;
-    rsum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[8 * t + e], a.scale_log2, negm));
         lsum += p;
         p_cur[t][e] = (__bf16)p;
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2 pr = {p_cur[t][2 * j], p_cur[t][2 * j + 1]};
-        rsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rsum, false);
-      }
-    }
     return lsum;
   };
 
@@ -293,10 +281,10 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   //   QK:   s_nxt = K Q^T of sub-tile u+1, rows [32 hn, +32) of `kn` (kQK);
   //   PV:   O^T += V^T P^T of sub-tile u-1, rows [32 hp, +32) of `vp` (kPV).
   // Returns true in a lane whose exponentials must be redone with a new
-  // maximum: its sum exceeds kSumLimit, so some p exceeds 2^kRescaleThreshold
-  // (inf or NaN while the row has no maximum yet, m_run = -inf).
+  // maximum: its sum exceeds kSumLimit (inf or NaN while the row has no
+  // maximum yet, m_run = -inf).
   auto body = [&](const f32x16& s_cur, f32x16& s_nxt, bf16x8 (&p_cur)[2], const bf16x8 (&p_prev)[2],
-                  const unsigned char* kn, int hn, const unsigned char* vp, int hp, float& lsum, float& rsum, auto exp_tag,
+                  const unsigned char* kn, int hn, const unsigned char* vp, int hp, float& lsum, auto exp_tag,
                   auto qk_tag, auto pv_tag) {
     constexpr bool kExp = decltype(exp_tag)::value;
     constexpr bool kQK = decltype(qk_tag)::value;
@@ -324,7 +312,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     if constexpr (!kExp) return false;
     // VALU stream.  -m_run is +inf while the row has no maximum: every p is
     // then inf (or NaN where masked) and the test below fails.
-    lsum = exps(s_cur, p_cur, -m_run, rsum);
+    lsum = exps(s_cur, p_cur, -m_run);
     // interleave: each MFMA followed by its share of LDS reads and VALU work
     constexpr int kMfma = (kQK ? NS : 0) + (kPV ? 2 * NDB : 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -346,11 +334,10 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     }
   };
   // Sub-iteration u: mask S(u) (first key at kpos) if it crosses this wave's
-  // diagonal and run the body.  Rarely (once at the start, and when the
-  // scores outgrow the running maximum) the exponentials are redone: the
-  // lazy maximum update raises a row's maximum only when the sub-tile's
-  // exceeds it by more than kRescaleThreshold, and the output, with PV(u-1)
-  // in, is rescaled to the new maximum.
+  // diagonal and run the body.  Rarely (on a row's first sub-tile, and when
+  // the scores outgrow the running maximum) the slow path raises every row
+  // maximum of the wave to its sub-tile maximum, rescales the output (PV(u-1)
+  // is in by then) and redoes the exponentials.
   auto sub = [&](int kpos, f32x16& s_cur, f32x16& s_nxt, bf16x8 (&p_cur)[2], const bf16x8 (&p_prev)[2],
                  const unsigned char* kn, int hn, const unsigned char* vp, int hp, auto exp_tag, auto qk_tag,
                  auto pv_tag) {
@@ -358,8 +345,8 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     if constexpr (kExp) {
       if (kpos + 31 > qw_pos) mask(s_cur, kpos);
     }
-    float lsum = 0.f, rsum = 0.f;
-    const bool redo = body(s_cur, s_nxt, p_cur, p_prev, kn, hn, vp, hp, lsum, rsum, exp_tag, qk_tag, pv_tag);
+    float lsum = 0.f;
+    const bool redo = body(s_cur, s_nxt, p_cur, p_prev, kn, hn, vp, hp, lsum, exp_tag, qk_tag, pv_tag);
     if constexpr (kExp) {
       float alpha = 1.f;
       if (__any(redo)) {
@@ -367,10 +354,10 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
         mx = xhalf_max(mx) * a.scale_log2;
-        const float m_new = (mx > m_run + kRescaleThreshold) ? mx : m_run;
+        const float m_new = fmaxf(m_run, mx);
         alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
-        lsum = exps(s_cur, p_cur, (m_run == neg_inf()) ? 0.f : -m_run, rsum);
+        lsum = exps(s_cur, p_cur, (m_run == neg_inf()) ? 0.f : -m_run);
         if (__any(alpha != 1.f)) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
@@ -379,7 +366,6 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
         }
       }
       l_lane = __builtin_fmaf(l_lane, alpha, lsum);
-      r_lane = __builtin_fmaf(r_lane, alpha, rsum);
     }
   };
   // Cursors at pair n: tm = tile n, tv = tile n+1, tk = tile n+2.
@@ -446,12 +432,9 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   }
 
   // ---- epilogue: normalise, LSE, merge, write ----
-  // LSE from the fp32 row sum; the output is normalised by the sum of the
-  // bf16 weights it was accumulated with
   const float l = xhalf_sum(l_lane);
-  const float r = xhalf_sum(r_lane);
   const float lse_j = (l > 0.f) ? (m_run + __log2f(l)) * kLn2 : neg_inf();
-  const float inv_l = (l > 0.f && r > 0.f) ? 1.f / r : 0.f;
+  const float inv_l = (l > 0.f) ? 1.f / l : 0.f;
   const size_t row = bh_q + qw_local + lq;
   float w_prev = 0.f, w_cur = inv_l, lse_new = lse_j;
   if (flags & kFlagMerge) {
