@@ -82,43 +82,52 @@ __device__ __forceinline__ int v_swz(int r) {
   return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
 
-// One direct-to-LDS load: each lane fetches 16 bytes at `src`; lane i's
-// bytes land at LDS address `lds_dst` + 16 i (`lds_dst` wave-uniform, in M0).
-// Issued as inline assembly so that the compiler's LDS-counter bookkeeping is
-// not made conservative by it: with a compiler-visible LDS DMA in flight every
-// ds_read wait becomes lgkmcnt(0).  Completion is tracked by hand instead:
-// wait_vmem_all() before the barrier that publishes the tile.  No other code
-// in this file uses M0.
-__device__ __forceinline__ void global_to_lds_16(const void* src, unsigned char* lds_dst) {
+// One direct-to-LDS load: each lane fetches the 16 bytes at `base` +
+// `voff` (`base` wave-uniform, in SGPRs; `voff` this lane's byte offset);
+// lane i's bytes land at LDS address `lds_dst` + 16 i (`lds_dst`
+// wave-uniform, in M0).  With a scalar base and a precomputed offset no
+// vector address arithmetic is spent per load.  Issued as inline assembly so
+// that the compiler's LDS-counter bookkeeping is not made conservative by
+// it: with a compiler-visible LDS DMA in flight every ds_read wait becomes
+// lgkmcnt(0).  Completion is tracked by hand instead: wait_vmem_all() before
+// the barrier that publishes the tile.  No other code in this file uses M0.
+__device__ __forceinline__ void global_to_lds_16(const void* base, unsigned voff, unsigned char* lds_dst) {
   const unsigned m0 = (unsigned)(uintptr_t)LDS_PTR(void, lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0) : "memory");
 }
 
 // Global -> LDS copy of one 64-key tile with the direct-to-LDS load: every
 // wave instruction j writes LDS bytes [1024 j, 1024 j + 1024), lane i the 16
 // bytes at 1024 j + 16 i, so each layout is produced by choosing which global
-// 16-B chunk lane i fetches.
-template <int D, int NW, bool kIsK>
-__device__ __forceinline__ void tile_to_lds(const uint16_t* __restrict__ rows, unsigned char* lds_buf, int wave_u,
-                                            int lane) {
-  constexpr int NC = D / 8;     // 16-B chunks per row = 1 KiB blocks per tile
-  constexpr int LPW = NC / NW;  // load instructions per wave per tile
+// 16-B chunk lane i fetches.  Wave w issues instructions j = i NW + w.
+template <int D, int NW>
+struct TileLoad {
+  static constexpr int NC = D / 8;     // 16-B chunks per row = 1 KiB blocks per tile
+  static constexpr int LPW = NC / NW;  // load instructions per wave per tile
   static_assert(LPW * NW == NC, "tile load must divide evenly");
+  unsigned off[LPW];  // byte offset, from the tile's first row, of this lane's chunk
+
+  __device__ __forceinline__ TileLoad(bool is_k, int wave_u, int lane) {
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int j = i * NW + wave_u;
-    int r, c;
-    if constexpr (kIsK) {
-      r = 32 * (j & 1) + (lane >> 1);
-      c = 2 * (j >> 1) + ((lane & 1) ^ k_half_swap(r));
-    } else {
-      const int slot = j * 64 + lane;
-      r = slot / NC;
-      c = (slot % NC) ^ v_swz<D>(r);
+    for (int i = 0; i < LPW; ++i) {
+      const int j = i * NW + wave_u;
+      int r, c;
+      if (is_k) {
+        r = 32 * (j & 1) + (lane >> 1);
+        c = 2 * (j >> 1) + ((lane & 1) ^ k_half_swap(r));
+      } else {
+        const int slot = j * 64 + lane;
+        r = slot / NC;
+        c = (slot % NC) ^ v_swz<D>(r);
+      }
+      off[i] = (unsigned)(r * D + 8 * c) * 2u;
     }
-    global_to_lds_16(rows + r * D + 8 * c, lds_buf + j * 1024);
   }
-}
+  __device__ __forceinline__ void operator()(const uint16_t* tile, unsigned char* lds_buf, int wave_u) const {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) global_to_lds_16(tile, off[i], lds_buf + (i * NW + wave_u) * 1024);
+  }
+};
 
 __device__ __forceinline__ void wait_vmem_all() {
   // s_waitcnt vmcnt(0): every global load this wave issued, including the
@@ -218,8 +227,9 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     if (t.left <= 0) t = chunk_after(t.c);  // rare: chunk boundary
     return t;
   };
-  auto load_k = [&](const Cursor& t, unsigned char* buf) { tile_to_lds<D, NW, true>(t.kp, buf, wave_u, lane); };
-  auto load_v = [&](const Cursor& t, unsigned char* buf) { tile_to_lds<D, NW, false>(t.vp, buf, wave_u, lane); };
+  const TileLoad<D, NW> k_loader(true, wave_u, lane), v_loader(false, wave_u, lane);
+  auto load_k = [&](const Cursor& t, unsigned char* buf) { k_loader(t.kp, buf, wave_u); };
+  auto load_v = [&](const Cursor& t, unsigned char* buf) { v_loader(t.vp, buf, wave_u); };
 
   // Q^T fragments: lane holds Q[row lq][16s + 8g .. +8]
   bf16x8 qf[NS];
@@ -313,6 +323,9 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     // VALU stream.  -m_run is +inf while the row has no maximum: every p is
     // then inf (or NaN where masked) and the test below fails.
     lsum = exps(s_cur, p_cur, -m_run);
+    // use the packed P here: otherwise the compiler sinks the conversions
+    // past the slow-path branch, out of the MFMA stream
+    asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]));
     // interleave: each MFMA followed by its share of LDS reads and VALU work
     constexpr int kMfma = (kQK ? NS : 0) + (kPV ? 2 * NDB : 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
