@@ -133,9 +133,9 @@ cp_status_t cp_attn_merge(float* o_acc, float* lse_acc,
                           hipStream_t stream);
 
 /* Workspace bytes cp_ring_attn_fwd needs: two staging slots, each for the K
- * and V blocks [B,H,Skv,D] bf16 of two ring steps (eight blocks), plus the
- * fp32 running output [B,H,Sq,D], each rounded up to 256 bytes.  Returns 0
- * for non-positive sizes. */
+ * and V blocks [B,H,Skv,D] bf16 of up to four ring steps (sixteen blocks),
+ * plus the fp32 running output [B,H,Sq,D], each rounded up to 256 bytes.
+ * Returns 0 for non-positive sizes. */
 size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq);
 
 /*
@@ -149,12 +149,12 @@ size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq);
  *             workspace on copy_stream, standing in for the peer-to-peer
  *             receive ([MLM] section 5: double buffering on a separate
  *             stream; [RAF] section 3: receive from the previous rank).
- *             After step 0, steps are computed two per kernel launch (one
- *             when a single step is left, or when a step has more than
- *             CP_MAX_CHUNKS / 2 chunks): a slot holds the blocks of the two
- *             steps of one launch, and the online softmax runs on across the
- *             two blocks, which equals merging the two steps' partial results
- *             by their log-sum-exp.
+ *             After step 0, the steps are computed in the fewest groups of
+ *             at most four steps and CP_MAX_CHUNKS chunks per kernel launch,
+ *             smaller groups first: a slot holds the blocks of one group,
+ *             and the online softmax runs on across the group's blocks,
+ *             which equals merging the steps' partial results by their
+ *             log-sum-exp.
  *   out       bf16 [B,H,Sq,D], lse fp32 [B,H,Sq]  (final results)
  *   workspace at least cp_ring_attn_workspace_bytes(B,H,Skv,D,Sq) bytes,
  *             256-byte aligned.

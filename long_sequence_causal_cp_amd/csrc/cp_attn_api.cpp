@@ -28,6 +28,10 @@
 
 using cpattn::StepArgs;
 
+// Most ring steps one step-kernel launch of cp_ring_attn_fwd covers; a
+// staging slot holds this many K/V blocks.
+constexpr int kStepsPerLaunch = 4;
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -296,7 +300,7 @@ size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq) {
   if (B <= 0 || H <= 0 || Skv <= 0 || D <= 0 || Sq <= 0) return 0;
   const size_t kv = round256((size_t)B * H * Skv * D * 2);
   const size_t o = round256((size_t)B * H * Sq * D * 4);
-  return 8 * kv + o;
+  return 4 * kStepsPerLaunch * kv + o;
 }
 
 cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const void* const* k_steps,
@@ -346,19 +350,28 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
   }
 
   // ---- plan ----
-  // Launches: step 0 on the caller's block, then the later steps two at a
-  // time (one launch attends the query block to both staged blocks; a single
-  // step when one is left over or when two steps' chunks exceed the launch's
-  // chunk table).  Staging is double buffered per launch: the blocks of
-  // launch g go to pair slot g % 2 on copy_stream while launch g-1 computes.
+  // Launches: step 0 on the caller's block, then steps 1 .. n_steps-1 in the
+  // fewest groups of at most kStepsPerLaunch steps (and at most
+  // CP_MAX_CHUNKS chunks), split as evenly as possible with the smaller
+  // groups first: one launch attends the query block to every staged block
+  // of its group.  Staging is double buffered per launch: the blocks of
+  // launch g go to slot g % 2 on copy_stream while launch g-1 computes, and
+  // a later group is never smaller, so its copies fit under the launch
+  // before it.
   const int nkv = kv_chunks_steps[0].n_chunks;
-  const int per = (2 * nkv <= CP_MAX_CHUNKS) ? 2 : 1;  // ring steps per staged launch
-  std::vector<int> l_first, l_count;                   // launches: first step, number of steps
+  const int per = std::max(1, std::min(kStepsPerLaunch, CP_MAX_CHUNKS / nkv));  // steps per staged launch
+  std::vector<int> l_first, l_count;  // launches: first step, number of steps
   l_first.push_back(0);
   l_count.push_back(1);
-  for (int j = 1; j < n_steps; j += per) {
-    l_first.push_back(j);
-    l_count.push_back(std::min(per, n_steps - j));
+  {
+    const int rest = n_steps - 1;
+    const int groups = (rest + per - 1) / per;
+    for (int g = 0, j = 1; g < groups; ++g) {
+      const int cnt = rest / groups + (g >= groups - rest % groups ? 1 : 0);
+      l_first.push_back(j);
+      l_count.push_back(cnt);
+      j += cnt;
+    }
   }
   const int n_launch = (int)l_first.size();
   const int nq = q_chunks->n_chunks;
@@ -376,13 +389,16 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
   for (int c = 0; c < nq; ++c)
     if (first[c] < 0) first[c] = last[c] = n_launch - 1;  // no key at all: write O = 0, LSE = -inf
 
-  // workspace: K pair slots [0,2) and [2,4), V pair slots [4,6) and [6,8) (in
-  // blocks of kv_slot bytes), then the fp32 running O
+  // workspace, in blocks of kv_slot bytes: K slot 0 [0, P), K slot 1 [P, 2P),
+  // V slot 0 [2P, 3P), V slot 1 [3P, 4P) with P = kStepsPerLaunch (a slot's
+  // blocks adjacent), then the fp32 running O
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const size_t kv_slot = round256(kv_bytes);
-  auto slot_k = [&](int g, int i) -> void* { return ws + (size_t)(2 * (g & 1) + i) * kv_slot; };
-  auto slot_v = [&](int g, int i) -> void* { return ws + (size_t)(4 + 2 * (g & 1) + i) * kv_slot; };
-  float* o_run = reinterpret_cast<float*>(ws + 8 * kv_slot);
+  auto slot_k = [&](int g, int i) -> void* { return ws + (size_t)(kStepsPerLaunch * (g & 1) + i) * kv_slot; };
+  auto slot_v = [&](int g, int i) -> void* {
+    return ws + (size_t)(2 * kStepsPerLaunch + kStepsPerLaunch * (g & 1) + i) * kv_slot;
+  };
+  float* o_run = reinterpret_cast<float*>(ws + 4 * kStepsPerLaunch * kv_slot);
 
   std::vector<hipEvent_t> ev;
   if ((st = get_events(2 + 2 * n_launch, ev)) != CP_OK) return st;

@@ -79,7 +79,7 @@ def test_zigzag_rejects_bad_arguments(lib, args):
 def test_workspace_bytes(lib):
     B, H, Skv, D, Sq = 1, 32, 4096, 128, 4096
     kv = B * H * Skv * D * 2
-    assert cb.cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq) == 8 * kv + B * H * Sq * D * 4
+    assert cb.cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq) == 16 * kv + B * H * Sq * D * 4
     assert cb.cp_ring_attn_workspace_bytes(1, 1, 64, 64, 64) % 256 == 0
     assert cb.cp_ring_attn_workspace_bytes(0, 1, 64, 64, 64) == 0
 
