@@ -581,16 +581,18 @@ __global__ void __launch_bounds__(256) merge_kernel(float* o_acc, float* lse_acc
 // step workgroup (248 VGPRs per wave) on every CU; the waves raise their
 // issue priority because they mostly wait on memory, and without it the
 // older step waves would starve them.  K is copied first, then V, in 16-byte
-// chunks; every lane keeps two chunks in flight.
+// chunks; every lane keeps two chunks in flight.  Loads and stores are
+// nontemporal, so the streamed block does not displace the step kernel's
+// K/V tiles from L2.
 __device__ __forceinline__ void copy_range(const u32x4* __restrict__ src, u32x4* __restrict__ dst, unsigned n,
                                            unsigned i, unsigned stride) {
   for (; i + stride < n; i += 2 * stride) {
-    const u32x4 x = src[i];
-    const u32x4 y = src[i + stride];
-    dst[i] = x;
-    dst[i + stride] = y;
+    const u32x4 x = __builtin_nontemporal_load(&src[i]);
+    const u32x4 y = __builtin_nontemporal_load(&src[i + stride]);
+    __builtin_nontemporal_store(x, &dst[i]);
+    __builtin_nontemporal_store(y, &dst[i + stride]);
   }
-  if (i < n) dst[i] = src[i];
+  if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
 }
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(8)))
     stage_copy_kernel(const u32x4* __restrict__ k_src, u32x4* __restrict__ k_dst, const u32x4* __restrict__ v_src,
