@@ -17,6 +17,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libcp_attn.so")
 
 SOURCES = ["cp_attn_kernels.hip", "cp_attn_api.cpp"]
+CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")  # measurement tool, its own executable
+CEILING_BIN = os.path.join(HERE, "mfma_ceiling")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -31,10 +33,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+def _run_hipcc(args, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *args, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,7 +45,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libcp_attn.so and the mfma_ceiling measurement tool; return the library path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    _run_hipcc([*FLAGS, "-I", os.path.join(ROOT, "include"), *srcs], LIB, verbose)
+    exe_flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    _run_hipcc([*exe_flags, CEILING_SRC], CEILING_BIN, verbose)
     return LIB
 
 
