@@ -202,6 +202,25 @@ def main():
     cp.cp_profile_enable(False)
     ms_per_step_instrumented = ek0.elapsed_time(ek1) / args.steps
 
+    # per-forward times (median), and the forward with every staging copy run
+    # in order on the launch stream (no copy/compute overlap)
+    def timed_each(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    def step_in_order():
+        cp.cp_ring_attn_fwd(q, q_tab, ks, vs, kv_tabs, out, lse, w.scale, ws, stream=stream, copy_stream=stream)
+
+    median_ms = statistics.median(timed_each(step, args.steps))
+    step_in_order()
+    no_overlap_ms = statistics.median(timed_each(step_in_order, args.steps))
+    props = torch.cuda.get_device_properties(dev)
+
     n_launch = len(kern_ms)
     assert n_launch > 0 and n_launch % args.steps == 0, (n_launch, args.steps)
     launches_per_step = n_launch // args.steps  # step-kernel launches per ring forward
@@ -273,7 +292,16 @@ def main():
             "flop_per_launch": per_launch_flops,
             "avg_launch_ms": round(avg_kernel_ms, 5),
             "ms_per_step_with_kernel_events": round(ms_per_step_instrumented, 5),
+            "kernel_ms_per_step": round(avg_kernel_ms * launches_per_step, 5),
         },
+        "timing": {
+            "ms_per_step_median": round(median_ms, 5),
+            "ms_per_step_no_overlap_median": round(no_overlap_ms, 5),
+            "note": "median over --steps forwards, each bracketed by HIP events; no_overlap runs every "
+                    "staging copy in order on the launch stream",
+        },
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count},
         "cpu_baseline": cpu,
         "check": {"max_abs_dout": eo, "max_abs_dlse": el},
     }

@@ -158,7 +158,10 @@ size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq);
  *   out       bf16 [B,H,Sq,D], lse fp32 [B,H,Sq]  (final results)
  *   workspace at least cp_ring_attn_workspace_bytes(B,H,Skv,D,Sq) bytes,
  *             256-byte aligned.
- *   copy_stream  a stream other than `stream` (not NULL).
+ *   copy_stream  a stream other than `stream`, on which the staging copies
+ *             overlap the compute; or `stream` itself, which runs every
+ *             copy in order before the launch that reads it (no overlap,
+ *             for measurement).  NULL only when `stream` is NULL too.
  * The copies for launch g+1 overlap the compute of launch g; the copy into a
  * slot waits until the launch that last read that slot has finished.  On entry
  * copy_stream waits for prior work on `stream`; before returning, `stream`

@@ -173,7 +173,7 @@ def cp_ring_attn_fwd(q, q_chunks: CpChunks, k_steps, v_steps, kv_chunks_steps, o
     vp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in v_steps])
     tables = (CpChunks * max(n, 1))(*kv_chunks_steps)
     if copy_stream is None:
-        raise ValueError("copy_stream is required (a torch.cuda.Stream other than stream)")
+        raise ValueError("copy_stream is required (a torch.cuda.Stream; stream itself runs the copies in order)")
     B, H, _, D = q.shape
     _check(load_library().cp_ring_attn_fwd(_ptr(q), ctypes.byref(q_chunks), kp, vp, tables, n,
                                            _ptr(out), _ptr(lse), B, H, D, float(softmax_scale),

@@ -327,8 +327,8 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4))
     return fail(CP_ERR_INVALID, "q, out must be 16-byte aligned and lse 4-byte aligned");
   if (!workspace || !aligned(workspace, 256)) return fail(CP_ERR_INVALID, "workspace NULL or not 256-byte aligned");
-  if (!copy_stream || copy_stream == stream)
-    return fail(CP_ERR_INVALID, "copy_stream must be a stream other than stream");
+  if (!copy_stream && stream)
+    return fail(CP_ERR_INVALID, "copy_stream is NULL (pass stream itself to run the copies in order)");
   const int Sq = q_chunks->n_chunks * q_chunks->chunk_len;
   const int Skv = kv_chunks_steps[0].n_chunks * kv_chunks_steps[0].chunk_len;
   const size_t need = cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq);

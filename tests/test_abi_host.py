@@ -155,8 +155,7 @@ def test_ring_validation(lib):
     assert _ring(lib, n_steps=65) == cb.CP_ERR_INVALID
     assert _ring(lib, ws_bytes=1000) == cb.CP_ERR_WORKSPACE
     assert "needed" in cb.cp_last_error()
-    assert _ring(lib, copy_stream=None) == cb.CP_ERR_INVALID
-    assert _ring(lib, copy_stream=ctypes.c_void_p(0x99), stream=ctypes.c_void_p(0x99)) == cb.CP_ERR_INVALID
+    assert _ring(lib, copy_stream=None, stream=ctypes.c_void_p(0x99)) == cb.CP_ERR_INVALID  # NULL beside a stream
     assert _ring(lib, kv_override=cb.CpChunks.make([0, 128, 192], 64)) == cb.CP_ERR_INVALID
     assert _ring(lib, workspace=ctypes.c_void_p(ALIGNED + 128)) == cb.CP_ERR_INVALID   # misaligned
     assert _ring(lib, workspace=fake(1)) == cb.CP_ERR_INVALID                           # overlaps out

@@ -276,7 +276,8 @@ def test_full_sequence_single_step():
 
 # ---------------------------------------------------------------- stream ordering
 def test_ring_unchanged_by_stream_delays():
-    """Delays injected on either stream must not change a single bit of the result."""
+    """Delays injected on either stream, or running the copies in order on the
+    compute stream, must not change a single bit of the result."""
     w = workloads.get("s16k_cp4")
     H = 4
     Q, K, V = workloads.make_qkv(w, H=H)
@@ -292,3 +293,7 @@ def test_ring_unchanged_by_stream_delays():
         out, lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV, copy_stream=side, kv_cache=cache)
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), where
+    # copy_stream == stream: every staging copy in order before its launch (no overlap)
+    out, lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV, stream=main, copy_stream=main, kv_cache=cache)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), "in order"
