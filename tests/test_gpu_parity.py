@@ -239,6 +239,25 @@ def test_contiguous_and_permuted_tables():
     assert (lse1 - lse2).abs().max().item() <= 1e-4
 
 
+def test_many_chunks_one_step_per_launch():
+    """Five interleaved chunks per rank and step: two steps' chunks exceed the
+    launch's chunk table, so the ring driver launches one step at a time."""
+    N, H, D, L, per_rank = 3, 2, 128, 256, 5
+    S = N * per_rank * L
+    Q, K, V = workloads.make_qkv_scaled((1, H, S, D), 97)
+    tabs = [cp.CpChunks.make([(i * N + r) * L for i in range(per_rank)], L) for r in range(N)]
+    for r in range(N):
+        q_tab = tabs[r]
+        kv_tabs = [tabs[(r - j) % N] for j in range(N)]
+        _announce("many chunks", r)
+        out, lse = run_ring(Q, K, V, q_tab, kv_tabs, 1 / math.sqrt(D), DEV)
+        torch.cuda.synchronize()
+        pos = positions(q_tab)
+        ro, rl = oracle_rows(Q, K, V, np.broadcast_to(pos, (1, H, len(pos))), 1 / math.sqrt(D))
+        eo, el = compare(out, lse, ro, rl)
+        assert eo <= OUT_TOL and el <= LSE_TOL, (r, eo, el)
+
+
 @pytest.mark.parametrize("D,L", [(128, 64), (64, 128), (64, 64), (128, 192)])
 def test_kernel_variants(D, L):
     """All four compiled step-kernel variants (D in {64,128}, 64- and 128-row blocks)."""
