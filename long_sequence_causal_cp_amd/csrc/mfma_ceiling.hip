@@ -1,8 +1,8 @@
 // Sustained bf16 MFMA throughput of the device, for the roofline of the step
 // kernel: every wave issues v_mfma_f32_32x32x16_bf16 back to back on register
 // operands (four independent accumulators, no memory traffic in the loop),
-// optionally each followed by independent v_fma_f32 (the VALU share the
-// step kernel's softmax needs).  The figure it prints is the dense bf16
+// optionally each followed by independent v_fma_f32, or by the step
+// kernel's softmax instruction mix.  The figure it prints is the dense bf16
 // rate the chip sustains under load, next to the published 2516.6 TFLOP/s.
 //
 // Build: part of long_sequence_causal_cp_amd.build (hipcc, gfx950).
@@ -27,10 +27,23 @@ constexpr double kFlopPerMfma = 2.0 * 32 * 32 * 16;
 
 // One MFMA and NF independent FMAs, in this order (one asm block, so the
 // compiler cannot regroup them).
+// NF = -1: the step kernel's softmax mix per MFMA instead of plain FMAs: one
+// FMA (scale and shift), one exp2, one add (row sum) and, every second MFMA,
+// one bf16 pack of two values.
+#define CEIL_SOFTMAX "v_fma_f32 %1, %1, %11, %12\nv_exp_f32 %2, %1\nv_add_f32 %3, %3, %2\n"
+#define CEIL_PACK "v_cvt_pk_bf16_f32 %4, %2, %3\n"
+
 template <int NF>
 __device__ __forceinline__ void mfma_step(f32x16& c, const bf16x8& a, const bf16x8& b, float& f0, float& f1, float& f2,
                                           float& f3, float& f4, float& f5, float& f6, float& f7, float m, float ad) {
   if constexpr (NF == 0) asm volatile(CEIL_MFMA : CEIL_OUTS(c) : CEIL_INS);
+  if constexpr (NF == -1) {
+    asm volatile(CEIL_MFMA CEIL_SOFTMAX : CEIL_OUTS(c) : CEIL_INS);
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %9, %10, %0\n"
+                 "v_fma_f32 %5, %5, %11, %12\nv_exp_f32 %6, %5\nv_add_f32 %7, %7, %6\n" CEIL_PACK
+                 : CEIL_OUTS(c)
+                 : CEIL_INS);
+  }
   if constexpr (NF == 4) asm volatile(CEIL_MFMA CEIL_FMA(1) CEIL_FMA(2) CEIL_FMA(3) CEIL_FMA(4) : CEIL_OUTS(c) : CEIL_INS);
   if constexpr (NF == 8)
     asm volatile(CEIL_MFMA CEIL_FMA(1) CEIL_FMA(2) CEIL_FMA(3) CEIL_FMA(4) CEIL_FMA(5) CEIL_FMA(6) CEIL_FMA(7)
@@ -74,11 +87,17 @@ int run(int n_cu, int waves_per_simd, float* out) {
   if (hipEventRecord(e1, 0) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) return 1;
   float ms = 0.f;
   if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) return 1;
-  const double n_mfma = (double)n_wg * 4 * kIters * 4;  // waves x MFMAs per wave
+  const int per_call = (NF == -1) ? 2 : 1;  // MFMAs per mfma_step
+  const double n_mfma = (double)n_wg * 4 * kIters * 4 * per_call;  // waves x MFMAs per wave
   const double tflops = n_mfma * kFlopPerMfma / (ms * 1e-3) / 1e12;
-  const double ns_per_mfma_simd = ms * 1e6 / ((double)kIters * 4 * waves_per_simd);
-  std::printf("%d wave(s)/SIMD, %d FMA per MFMA: %8.3f ms  %7.1f TFLOP/s  %6.2f ns per MFMA per SIMD\n",
-              waves_per_simd, NF, ms, tflops, ns_per_mfma_simd);
+  const double ns_per_mfma_simd = ms * 1e6 / ((double)kIters * 4 * per_call * waves_per_simd);
+  if (NF >= 0)
+    std::printf("%d wave(s)/SIMD, %d FMA per MFMA: %8.3f ms  %7.1f TFLOP/s  %6.2f ns per MFMA per SIMD\n",
+                waves_per_simd, NF, ms, tflops, ns_per_mfma_simd);
+  else
+    std::printf("%d wave(s)/SIMD, softmax mix per MFMA (fma, exp2, add, 1/2 bf16 pack): %8.3f ms  %7.1f TFLOP/s  "
+                "%6.2f ns per MFMA per SIMD\n",
+                waves_per_simd, ms, tflops, ns_per_mfma_simd);
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   return 0;
@@ -103,6 +122,7 @@ int main() {
   for (int w : {1, 2, 4}) rc |= run<0>(n_cu, w, out);
   for (int w : {2, 4}) rc |= run<4>(n_cu, w, out);
   for (int w : {2, 4}) rc |= run<8>(n_cu, w, out);
+  for (int w : {2, 4}) rc |= run<-1>(n_cu, w, out);
   (void)hipDeviceSynchronize();
   (void)hipFree(out);
   return rc;
