@@ -107,7 +107,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed forwards first; after host-side setup the GPU needs ~30 ms of load to reach steady clocks")
     ap.add_argument("--workload", default="s32k_cp8")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
