@@ -288,6 +288,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
+            "traffic_gb_per_s": (round(traffic / (avg_kernel_ms * 1e-3) / 1e9, 1) if traffic else None),
             "launches": n_launch,
             "launches_per_step": launches_per_step,
             "flop_per_launch": per_launch_flops,
