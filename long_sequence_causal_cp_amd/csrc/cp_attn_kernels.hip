@@ -200,8 +200,9 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     T += nv;
   }
   // Tiles are visited chunk by chunk.  A cursor names one tile: its chunk,
-  // how many visible tiles of that chunk remain from it, its row in the
-  // local K/V buffer and its absolute key position.  The chunk table is only
+  // how many visible tiles of that chunk remain from it, its absolute key
+  // position and its first K and V rows (every chunk has its own base, so a
+  // launch can span several ring steps' blocks).  The chunk table is only
   // read with constant indices, so it stays in scalar registers.
   int kv_start[kMaxChunks];
 #pragma unroll
