@@ -22,6 +22,10 @@ real-valued result, only the order of summation differs):
 
 with tau = 1/sqrt(D) and positions absolute in the full sequence.
 
+Gradients (``backward.py``): dQ, dK, dV of the same definition for an
+upstream dO, and the part one block of keys contributes to them (how a ring
+step's backward splits).
+
 Pins (tests marked "not gpu"): scalar brute force on tiny inputs, the closed
 forms for Q = 0 and for the first token, the merge invariant over arbitrary
 key splits, softmax normalisation, constant-V and key-shift invariance,
@@ -29,12 +33,14 @@ PyTorch's fp64 scaled-dot-product attention as an independent library case,
 and the zigzag worked example printed in [RAF] section 5.
 """
 from .attention import causal_attention_rows, masked_attention, to_f64
+from .backward import causal_attention_grad, masked_attention_grad
 from .merge import lse_merge
 from .zigzag import (zigzag_chunk_ids, local_positions, contiguous_positions,
                      ring_source, ring_kv_positions, visible_pairs)
 
 __all__ = [
     "causal_attention_rows", "masked_attention", "to_f64", "lse_merge",
+    "causal_attention_grad", "masked_attention_grad",
     "zigzag_chunk_ids", "local_positions", "contiguous_positions",
     "ring_source", "ring_kv_positions", "visible_pairs",
 ]
