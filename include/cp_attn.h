@@ -132,6 +132,60 @@ cp_status_t cp_attn_merge(float* o_acc, float* lse_acc,
                           int B, int H, int Sq, int D, void* out_bf16_or_null,
                           hipStream_t stream);
 
+/*
+ * Backward of one ring step ([MLM] section 2: the backward pass mirrors the
+ * forward, the K/V gradients travelling back along the ring; [MLM] section
+ * 5: forward and backward of one autograd function).  For a loss with
+ * gradient dO with respect to the output, with P_ij = exp(tau <q_i,k_j> -
+ * LSE_i) over the visible keys (position j <= i, absolute positions from the
+ * chunk tables) and 0 elsewhere, the K/V block of one step contributes
+ *
+ *     dV_j = sum_i P_ij dO_i,       dP_ij = <dO_i, v_j>,
+ *     dS_ij = P_ij (dP_ij - Delta_i),
+ *     dQ_i += tau sum_j dS_ij k_j,  dK_j = tau sum_i dS_ij q_i,
+ *
+ * where LSE and Delta_i = <dO_i, out_i> come from the complete forward (all
+ * steps).  A rank adds the dQ parts of its N steps; each block's dK and dV
+ * are summed over the ranks whose queries see it.
+ */
+enum { CP_BWD_DQ_ACCUMULATE = 1, CP_BWD_DKV_ACCUMULATE = 2 };
+
+/*
+ * Delta_i = sum_d dO[i][d] out[i][d] in fp32, for every row of the local
+ * queries (the forward's bf16 output and the upstream gradient).
+ *   out, d_out bf16 [B,H,Sq,D]; delta fp32 [B,H,Sq]
+ * Supported: D in {64, 128}; Sq >= 0 (Sq = 0 does nothing and accepts NULL
+ * pointers).  delta must not overlap the inputs.
+ */
+cp_status_t cp_attn_bwd_delta(const void* out, const void* d_out, float* delta,
+                              int B, int H, int Sq, int D, hipStream_t stream);
+
+/*
+ * Gradient contributions of one K/V block to the local queries and to the
+ * block itself.
+ *   q, d_out  bf16 [B,H,Sq,D] with table *q_chunks
+ *   k, v      bf16 [B,H,Skv,D] with table *kv_chunks
+ *   lse       fp32 [B,H,Sq], natural log, of the complete forward (-INFINITY:
+ *             the row has no visible key and contributes nothing)
+ *   delta     fp32 [B,H,Sq] from cp_attn_bwd_delta
+ *   dq        fp32 [B,H,Sq,D];  dk, dv  fp32 [B,H,Skv,D]
+ *   mode      bit CP_BWD_DQ_ACCUMULATE: dq += this block's part (else
+ *             dq := it); bit CP_BWD_DKV_ACCUMULATE: dk, dv += (else :=).
+ *             Every row of the outputs is written (with 0 where no visible
+ *             pair contributes).
+ * Two kernels on `stream`: one owns the dq rows, the other the dk/dv rows;
+ * no atomics, so results are deterministic.
+ * Supported: D in {64, 128}; B, H >= 1.  dq, dk, dv must not overlap each
+ * other or any input.  Errors as cp_attn_step_fwd; mode outside [0, 3] is
+ * CP_ERR_INVALID.
+ */
+cp_status_t cp_attn_step_bwd(const void* q, const void* k, const void* v, const void* d_out,
+                             const float* lse, const float* delta,
+                             float* dq, float* dk, float* dv,
+                             int B, int H, int D,
+                             const cp_chunks_t* q_chunks, const cp_chunks_t* kv_chunks,
+                             float softmax_scale, int mode, hipStream_t stream);
+
 /* Workspace bytes cp_ring_attn_fwd needs: two staging slots, each for the K
  * and V blocks [B,H,Skv,D] bf16 of up to four ring steps (sixteen blocks),
  * plus the fp32 running output [B,H,Sq,D], each rounded up to 256 bytes.
@@ -181,7 +235,8 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks,
 
 /*
  * Kernel timing for measurement.  While enabled, every attention-step kernel
- * launched by cp_attn_step_fwd / cp_ring_attn_fwd is bracketed by two HIP
+ * launched by cp_attn_step_fwd / cp_ring_attn_fwd, and each of the two
+ * kernels of cp_attn_step_bwd (dq first, then dk/dv), is bracketed by two HIP
  * events on its stream.  cp_profile_read waits for those events, writes up to
  * max_entries elapsed times (milliseconds, launch order) to kernel_ms and
  * their count to *n_entries, and clears the record.  At most 4096 launches

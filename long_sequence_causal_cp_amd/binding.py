@@ -21,6 +21,7 @@ CP_MAX_CHUNKS = 8
 CP_MAX_STEPS = 64
 CP_OK, CP_ERR_INVALID, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_ERR_HIP = range(5)
 CP_STEP_WRITE, CP_STEP_MERGE = 0, 1
+CP_BWD_DQ_ACCUMULATE, CP_BWD_DKV_ACCUMULATE = 1, 2
 STATUS_NAMES = {0: "CP_OK", 1: "CP_ERR_INVALID", 2: "CP_ERR_UNSUPPORTED", 3: "CP_ERR_WORKSPACE", 4: "CP_ERR_HIP"}
 
 
@@ -70,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "cp_zigzag_chunks": (i32, [i32, i32, i32, i32, pch, pch]),
         "cp_attn_step_fwd": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, pch, pch, f32, i32, vp]),
         "cp_attn_merge": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]),
+        "cp_attn_bwd_delta": (i32, [vp, vp, vp, i32, i32, i32, i32, vp]),
+        "cp_attn_step_bwd": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, pch, pch, f32, i32, vp]),
         "cp_ring_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "cp_ring_attn_fwd": (i32, [vp, pch, ctypes.POINTER(vp), ctypes.POINTER(vp), pch, i32, vp, vp,
                                    i32, i32, i32, f32, vp, sz, vp, vp]),
@@ -151,6 +154,29 @@ def cp_attn_merge(o_acc, lse_acc, o_part, lse_part, out=None, stream=None):
     B, H, Sq, D = o_acc.shape
     _check(load_library().cp_attn_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part),
                                         B, H, Sq, D, _ptr(out), _stream(stream)))
+
+
+def cp_attn_bwd_delta(out, d_out, delta, stream=None):
+    import torch
+    _need(out, torch.bfloat16, "out")
+    _need(d_out, torch.bfloat16, "d_out")
+    _need(delta, torch.float32, "delta")
+    B, H, Sq, D = out.shape
+    _check(load_library().cp_attn_bwd_delta(_ptr(out), _ptr(d_out), _ptr(delta), B, H, Sq, D, _stream(stream)))
+
+
+def cp_attn_step_bwd(q, k, v, d_out, lse, delta, dq, dk, dv, q_chunks: CpChunks, kv_chunks: CpChunks,
+                     softmax_scale: float, mode: int = 0, stream=None):
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_out, "d_out")):
+        _need(t, torch.bfloat16, n)
+    for t, n in ((lse, "lse"), (delta, "delta"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, torch.float32, n)
+    B, H, _, D = q.shape
+    _check(load_library().cp_attn_step_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(d_out), _ptr(lse), _ptr(delta),
+                                           _ptr(dq), _ptr(dk), _ptr(dv), B, H, D, ctypes.byref(q_chunks),
+                                           ctypes.byref(kv_chunks), float(softmax_scale), int(mode),
+                                           _stream(stream)))
 
 
 def cp_ring_attn_workspace_bytes(B: int, H: int, Skv: int, D: int, Sq: int) -> int:

@@ -155,7 +155,9 @@ Profiler& profiler() {
 }
 constexpr size_t kMaxTimed = 4096;
 
-hipError_t launch_step_timed(const StepArgs& a, int D, hipStream_t s) {
+// Run launch(s), bracketed by two timing events while profiling is enabled.
+template <class Launch>
+hipError_t timed(hipStream_t s, Launch&& launch) {
   Profiler& p = profiler();
   std::pair<hipEvent_t, hipEvent_t>* slot = nullptr;
   {
@@ -175,10 +177,14 @@ hipError_t launch_step_timed(const StepArgs& a, int D, hipStream_t s) {
   }
   hipError_t e;
   if (slot && (e = hipEventRecord(slot->first, s)) != hipSuccess) return e;
-  e = cpattn::launch_step(a, D, s);
+  e = launch(s);
   if (e != hipSuccess) return e;
   if (slot && (e = hipEventRecord(slot->second, s)) != hipSuccess) return e;
   return hipSuccess;
+}
+
+hipError_t launch_step_timed(const StepArgs& a, int D, hipStream_t s) {
+  return timed(s, [&](hipStream_t st) { return cpattn::launch_step(a, D, st); });
 }
 
 // ---------------- ring-driver event pool (per device) ----------------
@@ -292,6 +298,92 @@ cp_status_t cp_attn_merge(float* o_acc, float* lse_acc, const float* o_part, con
   hipError_t e = cpattn::launch_merge(o_acc, lse_acc, o_part, lse_part, static_cast<uint16_t*>(out_bf16_or_null),
                                       rows, D, stream);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  g_last_error.clear();
+  return CP_OK;
+}
+
+cp_status_t cp_attn_bwd_delta(const void* out, const void* d_out, float* delta, int B, int H, int Sq, int D,
+                              hipStream_t stream) {
+  if (B < 1 || H < 1 || Sq < 0) return fail(CP_ERR_INVALID, "B, H must be >= 1 and Sq >= 0");
+  if ((long long)B * H > (1LL << 24)) return fail(CP_ERR_INVALID, "B*H = %lld too large", (long long)B * H);
+  if (D != 64 && D != 128) return fail(CP_ERR_UNSUPPORTED, "head dim D = %d not built (64 or 128)", D);
+  if (Sq == 0) {  // nothing to compute; the pointers of empty tensors may be NULL
+    g_last_error.clear();
+    return CP_OK;
+  }
+  if (!out || !d_out || !delta) return fail(CP_ERR_INVALID, "out, d_out and delta must be non-NULL");
+  if (!aligned(out, 16) || !aligned(d_out, 16) || !aligned(delta, 4))
+    return fail(CP_ERR_INVALID, "out, d_out must be 16-byte aligned and delta 4-byte aligned");
+  const int64_t rows = (int64_t)B * H * Sq;
+  const size_t xb = (size_t)rows * D * 2, db = (size_t)rows * 4;
+  if (overlaps(delta, db, out, xb) || overlaps(delta, db, d_out, xb))
+    return fail(CP_ERR_INVALID, "delta must not overlap out or d_out");
+  hipError_t e = cpattn::launch_bwd_delta(static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(d_out),
+                                          delta, rows, D, stream);
+  if (e != hipSuccess) return hip_fail(e, "delta kernel launch");
+  g_last_error.clear();
+  return CP_OK;
+}
+
+cp_status_t cp_attn_step_bwd(const void* q, const void* k, const void* v, const void* d_out, const float* lse,
+                             const float* delta, float* dq, float* dk, float* dv, int B, int H, int D,
+                             const cp_chunks_t* q_chunks, const cp_chunks_t* kv_chunks, float softmax_scale, int mode,
+                             hipStream_t stream) {
+  cp_status_t st = check_common(B, H, D, softmax_scale);
+  if (st != CP_OK) return st;
+  if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
+  if ((st = check_chunks(kv_chunks, "kv_chunks")) != CP_OK) return st;
+  if (mode & ~(CP_BWD_DQ_ACCUMULATE | CP_BWD_DKV_ACCUMULATE)) return fail(CP_ERR_INVALID, "mode = %d unknown", mode);
+  if (!q || !k || !v || !d_out || !lse || !delta || !dq || !dk || !dv)
+    return fail(CP_ERR_INVALID, "every tensor argument must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_out, 16) || !aligned(dq, 16) ||
+      !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+    return fail(CP_ERR_INVALID, "q, k, v, d_out, dq, dk, dv must be 16-byte aligned and lse, delta 4-byte aligned");
+  const size_t BH = (size_t)B * H;
+  const size_t Sq = (size_t)q_chunks->n_chunks * q_chunks->chunk_len;
+  const size_t Skv = (size_t)kv_chunks->n_chunks * kv_chunks->chunk_len;
+  const size_t qb = BH * Sq * D * 2, kvb = BH * Skv * D * 2, lb = BH * Sq * 4;
+  const size_t dqb = BH * Sq * D * 4, dkb = BH * Skv * D * 4;
+  const void* ins[6] = {q, k, v, d_out, lse, delta};
+  const size_t insz[6] = {qb, kvb, kvb, qb, lb, lb};
+  const void* outs[3] = {dq, dk, dv};
+  const size_t outsz[3] = {dqb, dkb, dkb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return fail(CP_ERR_INVALID, "dq, dk, dv must not alias an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return fail(CP_ERR_INVALID, "dq, dk and dv must not overlap");
+  }
+
+  cpattn::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.dout = static_cast<const uint16_t*>(d_out);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.BH = (int)BH;
+  a.D = D;
+  a.Sq = (int)Sq;
+  a.Skv = (int)Skv;
+  a.q_chunk_len = q_chunks->chunk_len;
+  a.kv_chunk_len = kv_chunks->chunk_len;
+  a.n_q_chunks = q_chunks->n_chunks;
+  a.n_kv_chunks = kv_chunks->n_chunks;
+  for (int i = 0; i < a.n_q_chunks; ++i) a.q_start[i] = (int)q_chunks->start[i];
+  for (int i = 0; i < a.n_kv_chunks; ++i) a.kv_start[i] = (int)kv_chunks->start[i];
+  a.accumulate = mode;
+  a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = timed(stream, [&](hipStream_t s) { return cpattn::launch_bwd_dq(a, s); });
+  if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
+  e = timed(stream, [&](hipStream_t s) { return cpattn::launch_bwd_dkdv(a, s); });
+  if (e != hipSuccess) return hip_fail(e, "dk/dv kernel launch");
   g_last_error.clear();
   return CP_OK;
 }

@@ -43,6 +43,40 @@ struct StepArgs {
   float scale_log2;           // tau * log2(e)
 };
 
+// Everything one backward launch of one K/V block needs (both backward
+// kernels); passed by value.
+struct BwdArgs {
+  const uint16_t* q;     // bf16 [BH, Sq, D]
+  const uint16_t* dout;  // bf16 [BH, Sq, D], upstream gradient of the output
+  const uint16_t* k;     // bf16 [BH, Skv, D], one K/V block (its chunks concatenated)
+  const uint16_t* v;
+  const float* lse;      // fp32 [BH, Sq], natural log, of the complete forward
+  const float* delta;    // fp32 [BH, Sq], rowsum(dO * O) of the complete forward
+  float* dq;             // fp32 [BH, Sq, D]
+  float* dk;             // fp32 [BH, Skv, D], this block's rows
+  float* dv;
+  int BH, D;
+  int Sq, Skv;
+  int q_chunk_len, kv_chunk_len;
+  int n_q_chunks, n_kv_chunks;
+  int q_start[kMaxChunks];
+  int kv_start[kMaxChunks];
+  int accumulate;        // bit 0: dq += contribution (else =); bit 1: dk, dv += (else =)
+  int heads_per_xcd;     // > 0: keep each (b,h) on one XCD
+  float scale;           // tau
+  float scale_log2;      // tau * log2(e)
+};
+
+// Backward of one K/V block: the query-stationary dq kernel and the
+// key-stationary dk/dv kernel (rows and keys per workgroup for a chunk length).
+int bwd_dq_rows(int q_chunk_len);
+int bwd_dkdv_keys(int kv_chunk_len);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+// delta[r] = sum_d dout[r][d] * out[r][d] over `rows` rows of D bf16 values.
+hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, float* delta, int64_t rows, int D,
+                            hipStream_t stream);
+
 // Row-block height (queries per workgroup) the step kernel uses for a chunk length.
 int step_block_rows(int q_chunk_len);
 

@@ -160,3 +160,46 @@ def test_ring_validation(lib):
     assert _ring(lib, workspace=ctypes.c_void_p(ALIGNED + 128)) == cb.CP_ERR_INVALID   # misaligned
     assert _ring(lib, workspace=fake(1)) == cb.CP_ERR_INVALID                           # overlaps out
     assert _ring(lib, out=fake(10)) == cb.CP_ERR_INVALID                                # out overlaps K
+
+
+def _bwd(lib, D=128, mode=0, scale=0.088, B=1, H=2, qt=None, kvt=None, **ptrs):
+    qt = qt or cb.CpChunks.make([0, 192], 64)
+    kvt = kvt or cb.CpChunks.make([0, 192], 64)
+    p = dict(q=fake(0), k=fake(1), v=fake(2), d_out=fake(3), lse=fake(4), delta=fake(5), dq=fake(6), dk=fake(7),
+             dv=fake(8))
+    p.update(ptrs)
+    return lib.cp_attn_step_bwd(p["q"], p["k"], p["v"], p["d_out"], p["lse"], p["delta"], p["dq"], p["dk"],
+                                p["dv"], B, H, D, ctypes.byref(qt), ctypes.byref(kvt), scale, mode, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), cb.CP_ERR_UNSUPPORTED),
+    (dict(B=0), cb.CP_ERR_INVALID),
+    (dict(scale=float("nan")), cb.CP_ERR_INVALID),
+    (dict(mode=4), cb.CP_ERR_INVALID),
+    (dict(mode=-1), cb.CP_ERR_INVALID),
+    (dict(qt=cb.CpChunks.make([0, 192], 96)), cb.CP_ERR_INVALID),
+    (dict(kvt=cb.CpChunks.make([0, 32], 64)), cb.CP_ERR_INVALID),
+    (dict(dq=None), cb.CP_ERR_INVALID),
+    (dict(delta=None), cb.CP_ERR_INVALID),
+    (dict(dk=ctypes.c_void_p(ALIGNED + 7 * 1024 * MB + 8)), cb.CP_ERR_INVALID),    # misaligned
+    (dict(lse=ctypes.c_void_p(ALIGNED + 4 * 1024 * MB + 2)), cb.CP_ERR_INVALID),   # misaligned
+    (dict(dq=fake(0)), cb.CP_ERR_INVALID),                                         # dq aliases q
+    (dict(dv=fake(4)), cb.CP_ERR_INVALID),                                         # dv aliases lse
+    (dict(dv=fake(7)), cb.CP_ERR_INVALID),                                         # dv overlaps dk
+])
+def test_step_bwd_validation(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+    assert cb.cp_last_error()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 1, 64, 96), cb.CP_ERR_UNSUPPORTED),
+    ((0, 1, 64, 128), cb.CP_ERR_INVALID),
+    ((1, 1, -1, 128), cb.CP_ERR_INVALID),
+])
+def test_bwd_delta_validation(lib, args, status):
+    B, H, Sq, D = args
+    assert lib.cp_attn_bwd_delta(fake(0), fake(1), fake(2), B, H, Sq, D, None) == status
+    assert lib.cp_attn_bwd_delta(fake(0), fake(1), None, 1, 1, 64, 128, None) == cb.CP_ERR_INVALID
+    assert lib.cp_attn_bwd_delta(fake(0), fake(1), fake(0), 1, 1, 64, 128, None) == cb.CP_ERR_INVALID  # overlap

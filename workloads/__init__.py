@@ -26,7 +26,7 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_qkv", "make_qkv_scaled",
+__all__ = ["Workload", "WORKLOADS", "get", "make_qkv", "make_qkv_scaled", "make_grad_out",
            "sample_local_rows", "host_info"]
 
 
@@ -92,6 +92,19 @@ def make_qkv(w: Workload, seed: int | None = None, B: int | None = None,
     k = _draw(shape, gen)
     v = _draw(shape, gen)
     return q, k, v
+
+
+def make_grad_out(w: Workload, seed: int | None = None, B: int | None = None,
+                  H: int | None = None, S: int | None = None, D: int | None = None):
+    """Upstream gradient dO of the attention output, bf16 CPU [B, H, S, D].
+
+    Drawn like Q, K, V (standard normal in fp32, rounded to bf16) from its own
+    generator seeded with ``w.seed + 1000`` (or ``seed``), over the full
+    sequence in natural token order.
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed + 1000 if seed is None else seed)
+    return _draw((B or w.B, H or w.H, S or w.S, D or w.D), gen)
 
 
 def make_qkv_scaled(shape, seed: int, q_scale: float = 1.0, k_scale: float = 1.0,
