@@ -86,6 +86,182 @@ def cpu_baseline(w, rank, budget_s, Q, K, V):
     }
 
 
+def cpu_baseline_bwd(w, rank, budget_s, Q, K, V, kv_tabs):
+    """Time the fp64 gradient oracle on a bounded sample of the backward share.
+
+    The sample is (head, ring step) blocks taken in order: for each, the
+    oracle's forward rows of the rank's queries (needed for LSE and Delta) are
+    computed once per head, then the block's gradient contributions.  Only
+    the visible pairs of the gradient blocks count towards the rate.
+    """
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    pos = oracle.local_positions(w.S, w.cp, rank)
+    dO = workloads.make_grad_out(w)
+    done, pairs, t0 = 0, 0, time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            q, k, v, do = (oracle.to_f64(x[b, h]) for x in (Q, K, V, dO))
+            o, l = oracle.causal_attention_rows(q, k, v, pos, w.scale)
+            for j, t in enumerate(kv_tabs):
+                kpos = oracle.local_positions(w.S, w.cp, (rank - j) % w.cp)
+                oracle.masked_attention_grad(q[pos], pos, k[kpos], v[kpos], kpos, do[pos], o, l, w.scale)
+                pairs += int((kpos[None, :] <= pos[:, None]).sum())
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    info = workloads.host_info()
+    return {
+        "value": 10.0 * w.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": f"{done} (head, ring step) gradient blocks of rank {rank}'s {len(pos)} query rows, with "
+                  f"the forward rows they need: {pairs} visible pairs in {dt:.1f} s; {info['cpu_model']}",
+    }
+
+
+def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream, gather):
+    """The rank's backward share: Delta, then one cp_attn_step_bwd per ring step.
+
+    out and lse come from the GPU ring forward over the same inputs; dO is a
+    seeded bf16 N(0, 1) draw.  Step 0 writes dq and the local block's dk/dv;
+    steps j >= 1 accumulate dq and add into the travelling block's dk/dv (on a
+    real ring those would hold the partial sums of the ranks that saw the
+    block before).  Algorithmic flops: five products per visible pair (S, dP,
+    dV, dQ, dK), 10*D flop; the dq kernel's own work is S, dP and dQ (6*D per
+    pair), the dk/dv kernel's S, dP, dV and dK (8*D per pair).
+    """
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    import long_sequence_causal_cp_amd as cp
+
+    B, H, Sq, D = q.shape
+    Skv = ks[0].shape[2]
+    N, r = len(kv_tabs), args.rank
+    dev = q.device
+    do = gather(workloads.make_grad_out(w), q_tab)
+    delta = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    dq = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+    dks = [torch.zeros((B, H, Skv, D), dtype=torch.float32, device=dev) for _ in range(N)]
+    dvs = [torch.zeros((B, H, Skv, D), dtype=torch.float32, device=dev) for _ in range(N)]
+    acc = cp.CP_BWD_DQ_ACCUMULATE | cp.CP_BWD_DKV_ACCUMULATE
+
+    def step():
+        cp.cp_attn_bwd_delta(out, do, delta, stream=stream)
+        for j in range(N):
+            cp.cp_attn_step_bwd(q, ks[j], vs[j], do, lse, delta, dq, dks[j], dvs[j], q_tab, kv_tabs[j],
+                                w.scale, mode=0 if j == 0 else acc, stream=stream)
+
+    pairs_j = [visible_pairs(q_tab, [t]) for t in kv_tabs]
+    pairs = sum(pairs_j)
+    flops = 10.0 * D * B * H * pairs
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench bwd] {w.describe()} rank {r}: warmup {args.warmup} done", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    cp.cp_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern_ms = cp.cp_profile_read(8192)
+    cp.cp_profile_enable(False)
+    assert len(kern_ms) == 2 * N * args.steps, (len(kern_ms), N, args.steps)
+    dq_ms = statistics.fmean(kern_ms[0::2])
+    dkdv_ms = statistics.fmean(kern_ms[1::2])
+    dq_flop = 6.0 * D * B * H * pairs / N      # per launch, averaged over the ring steps
+    dkdv_flop = 8.0 * D * B * H * pairs / N
+    kernels = {
+        "dq": {"avg_launch_ms": round(dq_ms, 5), "flop_per_launch": dq_flop,
+               "achieved": round(dq_flop / (dq_ms * 1e-3) / 1e12, 2)},
+        "dkdv": {"avg_launch_ms": round(dkdv_ms, 5), "flop_per_launch": dkdv_flop,
+                 "achieved": round(dkdv_flop / (dkdv_ms * 1e-3) / 1e12, 2)},
+    }
+    dom = "dkdv" if dkdv_ms >= dq_ms else "dq"
+
+    # spot check against the oracle (outside the timed region): dq of four
+    # local rows, and dk/dv of four keys of the rank's own block (step 0)
+    pos = oracle.local_positions(w.S, N, r)
+    L = w.chunk_len
+    f64 = lambda X: oracle.to_f64(X[0, 0])
+    Qh, Kh, Vh = f64(Q), f64(K), f64(V)
+    dOh = oracle.to_f64(workloads.make_grad_out(w)[0, 0])
+    rows = np.array([0, L - 1, L, 2 * L - 1])
+    kmax = int(pos[rows].max()) + 1
+    o_r, l_r = oracle.causal_attention_rows(Qh, Kh, Vh, pos[rows], w.scale)
+    dq_ref, _, _ = oracle.masked_attention_grad(Qh[pos[rows]], pos[rows], Kh[:kmax], Vh[:kmax], np.arange(kmax),
+                                                dOh[pos[rows]], o_r, l_r, w.scale)
+    o_all, l_all = oracle.causal_attention_rows(Qh, Kh, Vh, pos, w.scale)
+    keys = np.array([0, L - 1, L, 2 * L - 1])
+    kpos0 = oracle.local_positions(w.S, N, (r - 0) % N)
+    _, dk_ref, dv_ref = oracle.masked_attention_grad(Qh[pos], pos, Kh[kpos0[keys]], Vh[kpos0[keys]], kpos0[keys],
+                                                     dOh[pos], o_all, l_all, w.scale)
+    cp.cp_attn_step_bwd(q, ks[0], vs[0], do, lse, delta, dq, dks[0], dvs[0], q_tab, kv_tabs[0], w.scale, mode=0,
+                        stream=stream)
+    for j in range(1, N):
+        cp.cp_attn_step_bwd(q, ks[j], vs[j], do, lse, delta, dq, dks[j], dvs[j], q_tab, kv_tabs[j], w.scale,
+                            mode=cp.CP_BWD_DQ_ACCUMULATE, stream=stream)
+    torch.cuda.synchronize()
+    rel = lambda got, ref: float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+    check = {"dq_rel": rel(dq[0, 0, rows].cpu().numpy(), dq_ref),
+             "dk_rel": rel(dks[0][0, 0, keys].cpu().numpy(), dk_ref),
+             "dv_rel": rel(dvs[0][0, 0, keys].cpu().numpy(), dv_ref)}
+    print(f"[bench bwd] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.1f} TFLOP/s; dq kernel "
+          f"{dq_ms:.4f} ms, dk/dv kernel {dkdv_ms:.4f} ms per launch; spot check {check}",
+          file=sys.stderr, flush=True)
+    res = {
+        "metric": "causal-effective attention backward TFLOP/s per CP-rank share; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": f"{w.name}: backward of causal ring attention, one rank's share (rank {r} of cp={N}), "
+                        f"B={B} H={H} D={D} S={w.S}, zigzag chunks of {L}, {N} ring steps of {Skv} keys",
+            "seq_len": w.S, "cp": N, "rank": r, "B": B, "H": H, "D": D,
+            "visible_pairs_per_head": pairs, "flop_per_step": flops, "wall_s_timed": round(wall, 4),
+        },
+        "roofline": {
+            "kernel": f"bwd_{dom}_kernel<128>", "bound": "mfma",
+            "achieved": kernels[dom]["achieved"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(kernels[dom]["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernels": kernels, "kernel_ms_per_step": round(N * (dq_ms + dkdv_ms), 5),
+        },
+        "cpu_baseline": cpu_baseline_bwd(w, r, args.cpu_budget, Q, K, V, kv_tabs) if args.cpu_budget > 0 else None,
+        "check": check,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def copy_probe(mib, reps):
     """Plain device copy of ``mib`` MiB (torch copy kernel), for counter calibration.
 
@@ -113,6 +289,8 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "step_kernel_s32k_cp8_traffic.json"))
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd: the ring forward (headline); bwd: the rank's backward ring steps")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB --steps times (counter calibration)")
     args = ap.parse_args()
@@ -165,6 +343,10 @@ def main():
     def step():
         cp.cp_ring_attn_fwd(q, q_tab, ks, vs, kv_tabs, out, lse, w.scale, ws, stream=stream,
                             copy_stream=copy_stream)
+
+    if args.pass_ == "bwd":
+        step()
+        return bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream, gather)
 
     pairs = visible_pairs(q_tab, kv_tabs)
     flops = 4.0 * D * B * H * pairs

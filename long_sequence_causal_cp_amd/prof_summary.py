@@ -25,12 +25,17 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(HERE, "csrc", "cp_attn_kernels.hip")
+# the step kernel's translation unit and the headers it includes
+KERNEL_SOURCES = tuple(os.path.join(HERE, "csrc", f)
+                       for f in ("cp_attn_kernels.hip", "cp_attn_tile.h", "cp_attn_internal.h"))
 
 
-def kernel_source_sha256(path: str = KERNEL_SOURCE) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_source_sha256(paths=KERNEL_SOURCES) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _rows(path):
