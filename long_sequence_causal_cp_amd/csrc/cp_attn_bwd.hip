@@ -349,6 +349,10 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     for (int st = 0; st < NS; ++st) {
       const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + k_base + st * 2048 + h * 1024);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
+    }
+    // dP after S (not interleaved): fewer operand reads in flight at once
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
       const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ob + k_base + st * 2048 + h * 1024);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[st], dp, 0, 0, 0);
     }
@@ -430,8 +434,12 @@ template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(const BwdArgs a) {
   dq_body<D, NW>(a);
 }
+// Two waves per SIMD at 256 keys per workgroup (8 waves): the register budget
+// is then 256 per lane, which the dk and dv accumulators (128) and the
+// stationary K and V fragments (64) nearly fill.
 template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_kernel(const BwdArgs a) {
   dkdv_body<D, NW>(a);
 }
 
@@ -463,7 +471,7 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const uint16_t* __restri
 int bwd_dq_rows(int q_chunk_len) {
   return (q_chunk_len % 256 == 0) ? 256 : (q_chunk_len % 128 == 0) ? 128 : 64;
 }
-int bwd_dkdv_keys(int kv_chunk_len) { return (kv_chunk_len % 128 == 0) ? 128 : 64; }
+int bwd_dkdv_keys(int kv_chunk_len) { return (kv_chunk_len % 256 == 0) ? 256 : (kv_chunk_len % 128 == 0) ? 128 : 64; }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const int bm = bwd_dq_rows(a.q_chunk_len);
@@ -488,10 +496,12 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk((unsigned)(2 * bn));  // one wave per 32 keys
   if (a.D == 128) {
-    if (bn == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128, 4>), g, blk, 0, stream, a);
+    if (bn == 256) hipLaunchKernelGGL((bwd_dkdv_kernel<128, 8>), g, blk, 0, stream, a);
+    else if (bn == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128, 4>), g, blk, 0, stream, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<128, 2>), g, blk, 0, stream, a);
   } else {
-    if (bn == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<64, 4>), g, blk, 0, stream, a);
+    if (bn == 256) hipLaunchKernelGGL((bwd_dkdv_kernel<64, 8>), g, blk, 0, stream, a);
+    else if (bn == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<64, 4>), g, blk, 0, stream, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<64, 2>), g, blk, 0, stream, a);
   }
   return hipGetLastError();
