@@ -130,15 +130,16 @@ def cpu_baseline_bwd(w, rank, budget_s, Q, K, V, kv_tabs):
 
 
 def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream, gather):
-    """The rank's backward share: Delta, then one cp_attn_step_bwd per ring step.
+    """The rank's backward share: one cp_ring_attn_bwd call.
 
     out and lse come from the GPU ring forward over the same inputs; dO is a
-    seeded bf16 N(0, 1) draw.  Step 0 writes dq and the local block's dk/dv;
-    steps j >= 1 accumulate dq and add into the travelling block's dk/dv (on a
-    real ring those would hold the partial sums of the ranks that saw the
-    block before).  Algorithmic flops: five products per visible pair (S, dP,
-    dV, dQ, dK), 10*D flop; the dq kernel's own work is S, dP and dQ (6*D per
-    pair), the dk/dv kernel's S, dP, dV and dK (8*D per pair).
+    seeded bf16 N(0, 1) draw.  The call computes Delta, then every ring step:
+    step 0 on the rank's own block writes its dK/dV; steps j >= 1 receive the
+    block and its travelling dK/dV partial sums into a staging slot, add this
+    rank's contribution and send the sums back (copies on a side stream).
+    dq accumulates over the steps.  Algorithmic flops: five products per
+    visible pair (S, dP, dV, dQ, dK), 10*D flop; the dq kernel's own work is
+    S, dP and dQ (6*D per pair), the dk/dv kernel's S, dP, dV and dK (8*D).
     """
     import numpy as np
     import torch
@@ -151,20 +152,17 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
     N, r = len(kv_tabs), args.rank
     dev = q.device
     do = gather(workloads.make_grad_out(w), q_tab)
-    delta = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
     dq = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
     dks = [torch.zeros((B, H, Skv, D), dtype=torch.float32, device=dev) for _ in range(N)]
     dvs = [torch.zeros((B, H, Skv, D), dtype=torch.float32, device=dev) for _ in range(N)]
-    acc = cp.CP_BWD_DQ_ACCUMULATE | cp.CP_BWD_DKV_ACCUMULATE
+    ws = torch.empty(cp.cp_ring_attn_bwd_workspace_bytes(B, H, Skv, D, Sq), dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream()
 
-    def step():
-        cp.cp_attn_bwd_delta(out, do, delta, stream=stream)
-        for j in range(N):
-            cp.cp_attn_step_bwd(q, ks[j], vs[j], do, lse, delta, dq, dks[j], dvs[j], q_tab, kv_tabs[j],
-                                w.scale, mode=0 if j == 0 else acc, stream=stream)
+    def step(cs=copy_stream):
+        cp.cp_ring_attn_bwd(q, q_tab, do, out, lse, ks, vs, kv_tabs, dks, dvs, dq, w.scale, ws, stream=stream,
+                            copy_stream=cs)
 
-    pairs_j = [visible_pairs(q_tab, [t]) for t in kv_tabs]
-    pairs = sum(pairs_j)
+    pairs = visible_pairs(q_tab, kv_tabs)
     flops = 10.0 * D * B * H * pairs
     for _ in range(args.warmup):
         step()
@@ -200,8 +198,23 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
     }
     dom = "dkdv" if dkdv_ms >= dq_ms else "dq"
 
+    def timed_each(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    median_ms = statistics.median(timed_each(step, args.steps))
+    no_overlap_ms = statistics.median(timed_each(lambda: step(stream), args.steps))
+
     # spot check against the oracle (outside the timed region): dq of four
-    # local rows, and dk/dv of four keys of the rank's own block (step 0)
+    # local rows, and dk/dv of four keys of the rank's own block (step 0
+    # writes them, so they hold this rank's contribution alone)
+    step()
+    torch.cuda.synchronize()
     pos = oracle.local_positions(w.S, N, r)
     L = w.chunk_len
     f64 = lambda X: oracle.to_f64(X[0, 0])
@@ -214,15 +227,9 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
                                                 dOh[pos[rows]], o_r, l_r, w.scale)
     o_all, l_all = oracle.causal_attention_rows(Qh, Kh, Vh, pos, w.scale)
     keys = np.array([0, L - 1, L, 2 * L - 1])
-    kpos0 = oracle.local_positions(w.S, N, (r - 0) % N)
+    kpos0 = oracle.local_positions(w.S, N, r)
     _, dk_ref, dv_ref = oracle.masked_attention_grad(Qh[pos], pos, Kh[kpos0[keys]], Vh[kpos0[keys]], kpos0[keys],
                                                      dOh[pos], o_all, l_all, w.scale)
-    cp.cp_attn_step_bwd(q, ks[0], vs[0], do, lse, delta, dq, dks[0], dvs[0], q_tab, kv_tabs[0], w.scale, mode=0,
-                        stream=stream)
-    for j in range(1, N):
-        cp.cp_attn_step_bwd(q, ks[j], vs[j], do, lse, delta, dq, dks[j], dvs[j], q_tab, kv_tabs[j], w.scale,
-                            mode=cp.CP_BWD_DQ_ACCUMULATE, stream=stream)
-    torch.cuda.synchronize()
     rel = lambda got, ref: float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
     check = {"dq_rel": rel(dq[0, 0, rows].cpu().numpy(), dq_ref),
              "dk_rel": rel(dks[0][0, 0, keys].cpu().numpy(), dk_ref),
@@ -255,6 +262,12 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
             "achieved": kernels[dom]["achieved"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(kernels[dom]["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
             "kernels": kernels, "kernel_ms_per_step": round(N * (dq_ms + dkdv_ms), 5),
+        },
+        "timing": {
+            "ms_per_step_median": round(median_ms, 5),
+            "ms_per_step_no_overlap_median": round(no_overlap_ms, 5),
+            "note": "median over --steps backward calls, each bracketed by HIP events; no_overlap runs every "
+                    "staging copy in order on the launch stream",
         },
         "cpu_baseline": cpu_baseline_bwd(w, r, args.cpu_budget, Q, K, V, kv_tabs) if args.cpu_budget > 0 else None,
         "check": check,

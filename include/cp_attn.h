@@ -233,10 +233,55 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream, hipStream_t copy_stream);
 
+/* Workspace bytes cp_ring_attn_bwd needs: Delta fp32 [B,H,Sq], then two
+ * staging slots, each for one step's K and V blocks (bf16 [B,H,Skv,D]) and
+ * the dK and dV partial sums that travel with it (fp32 [B,H,Skv,D]), each
+ * rounded up to 256 bytes.  Returns 0 for non-positive sizes. */
+size_t cp_ring_attn_bwd_workspace_bytes(int B, int H, int Skv, int D, int Sq);
+
+/*
+ * Backward of a rank's whole share, replayed on one GPU ([MLM] section 2:
+ * the backward pass mirrors the forward; the K/V blocks go around the ring
+ * again and each block's gradients travel with it, collecting every rank's
+ * contribution).
+ *   q, d_out, out  bf16 [B,H,Sq,D] with table *q_chunks; out and lse are the
+ *             complete forward results (cp_ring_attn_fwd)
+ *   lse       fp32 [B,H,Sq]
+ *   k_steps[j], v_steps[j]  as for cp_ring_attn_fwd (ring order, step 0 the
+ *             rank's own block)
+ *   dk_steps[j], dv_steps[j]  host array of n_steps device pointers, fp32
+ *             [B,H,Skv,D]: the partial sums of dK and dV of step j's block.
+ *             They are read and added to where dkv_accumulate[j] != 0, else
+ *             overwritten with this rank's contribution.
+ *   dkv_accumulate  host array [n_steps], or NULL for the ring's own pattern:
+ *             step 0 (the block's first visit) writes, later steps add.
+ *   dq        fp32 [B,H,Sq,D]: written, the sum of every step's part.
+ * Delta = rowsum(d_out * out) goes to the workspace first.  Step 0 reads its
+ * K/V in place and writes dk_steps[0], dv_steps[0] directly.  For j >= 1, on
+ * copy_stream, the block and (when adding) its partial sums are copied into
+ * staging slot (j-1) % 2 (the receive), the kernels on `stream` update the
+ * slot's partial sums, and they are copied back to dk_steps[j], dv_steps[j]
+ * (the send).  Step j+2's receive into the same slot follows that send on
+ * copy_stream.  Stream semantics and copy_stream == stream as for
+ * cp_ring_attn_fwd: on return `stream` is ordered after every copy.
+ * Supported: D in {64, 128}.  dq, every dK/dV buffer and the workspace must
+ * not overlap one another or any input.  Errors as cp_ring_attn_fwd.
+ */
+cp_status_t cp_ring_attn_bwd(const void* q, const cp_chunks_t* q_chunks,
+                             const void* d_out, const void* out, const float* lse,
+                             const void* const* k_steps, const void* const* v_steps,
+                             const cp_chunks_t* kv_chunks_steps, int n_steps,
+                             float* const* dk_steps, float* const* dv_steps,
+                             const int* dkv_accumulate, float* dq,
+                             int B, int H, int D, float softmax_scale,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, hipStream_t copy_stream);
+
 /*
  * Kernel timing for measurement.  While enabled, every attention-step kernel
  * launched by cp_attn_step_fwd / cp_ring_attn_fwd, and each of the two
- * kernels of cp_attn_step_bwd (dq first, then dk/dv), is bracketed by two HIP
+ * kernels of cp_attn_step_bwd and of every step of cp_ring_attn_bwd (dq
+ * first, then dk/dv), is bracketed by two HIP
  * events on its stream.  cp_profile_read waits for those events, writes up to
  * max_entries elapsed times (milliseconds, launch order) to kernel_ms and
  * their count to *n_entries, and clears the record.  At most 4096 launches

@@ -76,6 +76,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "cp_ring_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "cp_ring_attn_fwd": (i32, [vp, pch, ctypes.POINTER(vp), ctypes.POINTER(vp), pch, i32, vp, vp,
                                    i32, i32, i32, f32, vp, sz, vp, vp]),
+        "cp_ring_attn_bwd_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "cp_ring_attn_bwd": (i32, [vp, pch, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), pch, i32,
+                                   ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i32), vp,
+                                   i32, i32, i32, f32, vp, sz, vp, vp]),
         "cp_profile_enable": (i32, [i32]),
         "cp_profile_read": (i32, [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(ctypes.c_int)]),
     }
@@ -205,6 +209,41 @@ def cp_ring_attn_fwd(q, q_chunks: CpChunks, k_steps, v_steps, kv_chunks_steps, o
                                            _ptr(out), _ptr(lse), B, H, D, float(softmax_scale),
                                            _ptr(workspace), workspace.numel(), _stream(stream),
                                            _stream(copy_stream)))
+
+
+def cp_ring_attn_bwd_workspace_bytes(B: int, H: int, Skv: int, D: int, Sq: int) -> int:
+    return int(load_library().cp_ring_attn_bwd_workspace_bytes(B, H, Skv, D, Sq))
+
+
+def cp_ring_attn_bwd(q, q_chunks: CpChunks, d_out, out, lse, k_steps, v_steps, kv_chunks_steps, dk_steps, dv_steps,
+                     dq, softmax_scale: float, workspace, dkv_accumulate=None, stream=None, copy_stream=None):
+    import torch
+    for t, n in ((q, "q"), (d_out, "d_out"), (out, "out")):
+        _need(t, torch.bfloat16, n)
+    _need(lse, torch.float32, "lse")
+    _need(dq, torch.float32, "dq")
+    _need(workspace, torch.uint8, "workspace")
+    n = len(k_steps)
+    if not (len(v_steps) == len(kv_chunks_steps) == len(dk_steps) == len(dv_steps) == n):
+        raise ValueError("k_steps, v_steps, kv_chunks_steps, dk_steps and dv_steps must have the same length")
+    for t in list(k_steps) + list(v_steps):
+        _need(t, torch.bfloat16, "k/v step")
+    for t in list(dk_steps) + list(dv_steps):
+        _need(t, torch.float32, "dk/dv step")
+    ptrs = lambda ts: (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in ts])
+    tables = (CpChunks * max(n, 1))(*kv_chunks_steps)
+    acc = None
+    if dkv_accumulate is not None:
+        if len(dkv_accumulate) != n:
+            raise ValueError("dkv_accumulate must have one entry per step")
+        acc = (ctypes.c_int * n)(*[int(bool(x)) for x in dkv_accumulate])
+    if copy_stream is None:
+        raise ValueError("copy_stream is required (a torch.cuda.Stream; stream itself runs the copies in order)")
+    B, H, _, D = q.shape
+    _check(load_library().cp_ring_attn_bwd(_ptr(q), ctypes.byref(q_chunks), _ptr(d_out), _ptr(out), _ptr(lse),
+                                           ptrs(k_steps), ptrs(v_steps), tables, n, ptrs(dk_steps), ptrs(dv_steps),
+                                           acc, _ptr(dq), B, H, D, float(softmax_scale), _ptr(workspace),
+                                           workspace.numel(), _stream(stream), _stream(copy_stream)))
 
 
 def cp_profile_enable(enable: bool):

@@ -187,6 +187,45 @@ hipError_t launch_step_timed(const StepArgs& a, int D, hipStream_t s) {
   return timed(s, [&](hipStream_t st) { return cpattn::launch_step(a, D, st); });
 }
 
+// Launch arguments of the two backward kernels for one K/V block.
+cpattn::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* d_out, const float* lse,
+                         const float* delta, float* dq, float* dk, float* dv, int B, int H, int D,
+                         const cp_chunks_t* qc, const cp_chunks_t* kvc, float scale, int mode) {
+  cpattn::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.dout = static_cast<const uint16_t*>(d_out);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.BH = B * H;
+  a.D = D;
+  a.Sq = qc->n_chunks * qc->chunk_len;
+  a.Skv = kvc->n_chunks * kvc->chunk_len;
+  a.q_chunk_len = qc->chunk_len;
+  a.kv_chunk_len = kvc->chunk_len;
+  a.n_q_chunks = qc->n_chunks;
+  a.n_kv_chunks = kvc->n_chunks;
+  for (int i = 0; i < a.n_q_chunks; ++i) a.q_start[i] = (int)qc->start[i];
+  for (int i = 0; i < a.n_kv_chunks; ++i) a.kv_start[i] = (int)kvc->start[i];
+  a.accumulate = mode;
+  a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+// Both backward kernels of one block (dq rows, then dk/dv rows), each timed.
+hipError_t launch_bwd_pair(const cpattn::BwdArgs& a, hipStream_t stream) {
+  hipError_t e = timed(stream, [&](hipStream_t s) { return cpattn::launch_bwd_dq(a, s); });
+  if (e != hipSuccess) return e;
+  return timed(stream, [&](hipStream_t s) { return cpattn::launch_bwd_dkdv(a, s); });
+}
+
 // ---------------- ring-driver event pool (per device) ----------------
 std::mutex g_pool_mu;
 std::map<int, std::vector<hipEvent_t>> g_pools;
@@ -355,35 +394,10 @@ cp_status_t cp_attn_step_bwd(const void* q, const void* k, const void* v, const 
       if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return fail(CP_ERR_INVALID, "dq, dk and dv must not overlap");
   }
 
-  cpattn::BwdArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.q = static_cast<const uint16_t*>(q);
-  a.dout = static_cast<const uint16_t*>(d_out);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.lse = lse;
-  a.delta = delta;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.BH = (int)BH;
-  a.D = D;
-  a.Sq = (int)Sq;
-  a.Skv = (int)Skv;
-  a.q_chunk_len = q_chunks->chunk_len;
-  a.kv_chunk_len = kv_chunks->chunk_len;
-  a.n_q_chunks = q_chunks->n_chunks;
-  a.n_kv_chunks = kv_chunks->n_chunks;
-  for (int i = 0; i < a.n_q_chunks; ++i) a.q_start[i] = (int)q_chunks->start[i];
-  for (int i = 0; i < a.n_kv_chunks; ++i) a.kv_start[i] = (int)kv_chunks->start[i];
-  a.accumulate = mode;
-  a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
-  a.scale = softmax_scale;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipError_t e = timed(stream, [&](hipStream_t s) { return cpattn::launch_bwd_dq(a, s); });
-  if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
-  e = timed(stream, [&](hipStream_t s) { return cpattn::launch_bwd_dkdv(a, s); });
-  if (e != hipSuccess) return hip_fail(e, "dk/dv kernel launch");
+  const cpattn::BwdArgs a = bwd_args(q, k, v, d_out, lse, delta, dq, dk, dv, B, H, D, q_chunks, kv_chunks,
+                                     softmax_scale, mode);
+  hipError_t e = launch_bwd_pair(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   g_last_error.clear();
   return CP_OK;
 }
@@ -548,6 +562,143 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
       if (l >= 1) HIP_TRY(hipEventRecord(released[l], stream), "hipEventRecord");
       if (l + 2 >= 3 && (st = stage(l + 2)) != CP_OK) return st;
     }
+  }
+  HIP_TRY(hipEventRecord(ev_done, copy_stream), "hipEventRecord");
+  HIP_TRY(hipStreamWaitEvent(stream, ev_done, 0), "hipStreamWaitEvent");
+#undef HIP_TRY
+  g_last_error.clear();
+  return CP_OK;
+}
+
+size_t cp_ring_attn_bwd_workspace_bytes(int B, int H, int Skv, int D, int Sq) {
+  if (B <= 0 || H <= 0 || Skv <= 0 || D <= 0 || Sq <= 0) return 0;
+  const size_t kv = round256((size_t)B * H * Skv * D * 2);
+  const size_t g = round256((size_t)B * H * Skv * D * 4);
+  const size_t delta = round256((size_t)B * H * Sq * 4);
+  return delta + 2 * (2 * kv + 2 * g);
+}
+
+cp_status_t cp_ring_attn_bwd(const void* q, const cp_chunks_t* q_chunks, const void* d_out, const void* out,
+                             const float* lse, const void* const* k_steps, const void* const* v_steps,
+                             const cp_chunks_t* kv_chunks_steps, int n_steps, float* const* dk_steps,
+                             float* const* dv_steps, const int* dkv_accumulate, float* dq, int B, int H, int D,
+                             float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             hipStream_t copy_stream) {
+  cp_status_t st = check_common(B, H, D, softmax_scale);
+  if (st != CP_OK) return st;
+  if (n_steps < 1 || n_steps > CP_MAX_STEPS)
+    return fail(CP_ERR_INVALID, "n_steps = %d outside [1, %d]", n_steps, CP_MAX_STEPS);
+  if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
+  if (!k_steps || !v_steps || !kv_chunks_steps || !dk_steps || !dv_steps)
+    return fail(CP_ERR_INVALID, "k_steps, v_steps, kv_chunks_steps, dk_steps, dv_steps must be non-NULL");
+  for (int j = 0; j < n_steps; ++j) {
+    char name[48];
+    snprintf(name, sizeof(name), "kv_chunks_steps[%d]", j);
+    if ((st = check_chunks(&kv_chunks_steps[j], name)) != CP_OK) return st;
+    if (kv_chunks_steps[j].n_chunks != kv_chunks_steps[0].n_chunks ||
+        kv_chunks_steps[j].chunk_len != kv_chunks_steps[0].chunk_len)
+      return fail(CP_ERR_INVALID, "every step's K/V table must have the same n_chunks and chunk_len");
+    if (!k_steps[j] || !v_steps[j] || !dk_steps[j] || !dv_steps[j] || !aligned(k_steps[j], 16) ||
+        !aligned(v_steps[j], 16) || !aligned(dk_steps[j], 16) || !aligned(dv_steps[j], 16))
+      return fail(CP_ERR_INVALID, "step %d: K, V, dK or dV NULL or not 16-byte aligned", j);
+  }
+  if (!q || !d_out || !out || !lse || !dq) return fail(CP_ERR_INVALID, "q, d_out, out, lse and dq must be non-NULL");
+  if (!aligned(q, 16) || !aligned(d_out, 16) || !aligned(out, 16) || !aligned(dq, 16) || !aligned(lse, 4))
+    return fail(CP_ERR_INVALID, "q, d_out, out, dq must be 16-byte aligned and lse 4-byte aligned");
+  if (!workspace || !aligned(workspace, 256)) return fail(CP_ERR_INVALID, "workspace NULL or not 256-byte aligned");
+  if (!copy_stream && stream)
+    return fail(CP_ERR_INVALID, "copy_stream is NULL (pass stream itself to run the copies in order)");
+  const int Sq = q_chunks->n_chunks * q_chunks->chunk_len;
+  const int Skv = kv_chunks_steps[0].n_chunks * kv_chunks_steps[0].chunk_len;
+  const size_t need = cp_ring_attn_bwd_workspace_bytes(B, H, Skv, D, Sq);
+  if (workspace_bytes < need)
+    return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t BH = (size_t)B * H;
+  const size_t kv_bytes = BH * Skv * D * 2, g_bytes = BH * Skv * D * 4;
+  const size_t q_bytes = BH * Sq * D * 2, dq_bytes = BH * Sq * D * 4, lse_bytes = BH * Sq * 4;
+  // outputs (dq, every dK/dV, the workspace) must not overlap each other or any input
+  std::vector<std::pair<const void*, size_t>> ins = {{q, q_bytes}, {d_out, q_bytes}, {out, q_bytes}, {lse, lse_bytes}};
+  std::vector<std::pair<const void*, size_t>> outs = {{workspace, need}, {dq, dq_bytes}};
+  for (int j = 0; j < n_steps; ++j) {
+    ins.emplace_back(k_steps[j], kv_bytes);
+    ins.emplace_back(v_steps[j], kv_bytes);
+    outs.emplace_back(dk_steps[j], g_bytes);
+    outs.emplace_back(dv_steps[j], g_bytes);
+  }
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const auto& in : ins)
+      if (overlaps(outs[i].first, outs[i].second, in.first, in.second))
+        return fail(CP_ERR_INVALID, "dq, dK/dV buffers and workspace must not overlap an input");
+    for (size_t k = i + 1; k < outs.size(); ++k)
+      if (overlaps(outs[i].first, outs[i].second, outs[k].first, outs[k].second))
+        return fail(CP_ERR_INVALID, "dq, the dK/dV buffers of every step and the workspace must not overlap");
+  }
+
+  // workspace: Delta, then two slots of (K, V, dK, dV); step j >= 1 uses slot (j - 1) % 2
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* delta = reinterpret_cast<float*>(ws);
+  unsigned char* slots = ws + round256(lse_bytes);
+  const size_t kv_r = round256(kv_bytes), g_r = round256(g_bytes);
+  const size_t slot_bytes = 2 * kv_r + 2 * g_r;
+  auto slot_k = [&](int j) -> void* { return slots + (size_t)((j - 1) & 1) * slot_bytes; };
+  auto slot_v = [&](int j) -> void* { return slots + (size_t)((j - 1) & 1) * slot_bytes + kv_r; };
+  auto slot_dk = [&](int j) -> float* {
+    return reinterpret_cast<float*>(slots + (size_t)((j - 1) & 1) * slot_bytes + 2 * kv_r);
+  };
+  auto slot_dv = [&](int j) -> float* {
+    return reinterpret_cast<float*>(slots + (size_t)((j - 1) & 1) * slot_bytes + 2 * kv_r + g_r);
+  };
+  auto adds = [&](int j) { return dkv_accumulate ? dkv_accumulate[j] != 0 : j > 0; };
+
+  std::vector<hipEvent_t> ev;
+  if ((st = get_events(2 + 2 * n_steps, ev)) != CP_OK) return st;
+  hipEvent_t ev_entry = ev[0], ev_done = ev[1];
+  hipEvent_t* copied = &ev[2];              // per step: its block and partial sums are in the slot
+  hipEvent_t* computed = &ev[2 + n_steps];  // per step: its kernels are done with the slot
+
+  hipError_t e;
+#define HIP_TRY(call, what)                                   \
+  do {                                                        \
+    if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
+  } while (0)
+  // receive of step j >= 1 on copy_stream: the block, and the partial sums it carries
+  auto receive = [&](int j) -> cp_status_t {
+    HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k(j), v_steps[j], slot_v(j), kv_bytes, copy_stream),
+            "staging copy launch");
+    if (adds(j))
+      HIP_TRY(cpattn::launch_stage_copy(dk_steps[j], slot_dk(j), dv_steps[j], slot_dv(j), g_bytes, copy_stream),
+              "staging copy launch");
+    HIP_TRY(hipEventRecord(copied[j], copy_stream), "hipEventRecord");
+    return CP_OK;
+  };
+
+  HIP_TRY(hipEventRecord(ev_entry, stream), "hipEventRecord");
+  HIP_TRY(hipStreamWaitEvent(copy_stream, ev_entry, 0), "hipStreamWaitEvent");
+  for (int j = 1; j < n_steps && j <= 2; ++j)
+    if ((st = receive(j)) != CP_OK) return st;
+  HIP_TRY(cpattn::launch_bwd_delta(static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(d_out), delta,
+                                   (int64_t)BH * Sq, D, stream),
+          "delta kernel launch");
+  for (int j = 0; j < n_steps; ++j) {
+    const int mode = (j > 0 ? CP_BWD_DQ_ACCUMULATE : 0) | (adds(j) ? CP_BWD_DKV_ACCUMULATE : 0);
+    cpattn::BwdArgs a;
+    if (j == 0) {  // the rank's own block, in place
+      a = bwd_args(q, k_steps[0], v_steps[0], d_out, lse, delta, dq, dk_steps[0], dv_steps[0], B, H, D, q_chunks,
+                   &kv_chunks_steps[0], softmax_scale, mode);
+    } else {
+      HIP_TRY(hipStreamWaitEvent(stream, copied[j], 0), "hipStreamWaitEvent");
+      a = bwd_args(q, slot_k(j), slot_v(j), d_out, lse, delta, dq, slot_dk(j), slot_dv(j), B, H, D, q_chunks,
+                   &kv_chunks_steps[j], softmax_scale, mode);
+    }
+    HIP_TRY(launch_bwd_pair(a, stream), "backward kernel launch");
+    if (j == 0) continue;
+    // send of step j: the updated partial sums leave the slot; then the slot
+    // takes step j + 2's receive (copy_stream order keeps the two apart)
+    HIP_TRY(hipEventRecord(computed[j], stream), "hipEventRecord");
+    HIP_TRY(hipStreamWaitEvent(copy_stream, computed[j], 0), "hipStreamWaitEvent");
+    HIP_TRY(cpattn::launch_stage_copy(slot_dk(j), dk_steps[j], slot_dv(j), dv_steps[j], g_bytes, copy_stream),
+            "staging copy launch");
+    if (j + 2 < n_steps && (st = receive(j + 2)) != CP_OK) return st;
   }
   HIP_TRY(hipEventRecord(ev_done, copy_stream), "hipEventRecord");
   HIP_TRY(hipStreamWaitEvent(stream, ev_done, 0), "hipStreamWaitEvent");

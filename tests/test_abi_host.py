@@ -203,3 +203,45 @@ def test_bwd_delta_validation(lib, args, status):
     assert lib.cp_attn_bwd_delta(fake(0), fake(1), fake(2), B, H, Sq, D, None) == status
     assert lib.cp_attn_bwd_delta(fake(0), fake(1), None, 1, 1, 64, 128, None) == cb.CP_ERR_INVALID
     assert lib.cp_attn_bwd_delta(fake(0), fake(1), fake(0), 1, 1, 64, 128, None) == cb.CP_ERR_INVALID  # overlap
+
+
+def test_ring_bwd_workspace_bytes(lib):
+    B, H, Skv, D, Sq = 1, 32, 4096, 128, 4096
+    kv = B * H * Skv * D * 2
+    assert cb.cp_ring_attn_bwd_workspace_bytes(B, H, Skv, D, Sq) == B * H * Sq * 4 + 2 * (2 * kv + 4 * kv)
+    assert cb.cp_ring_attn_bwd_workspace_bytes(1, 1, 64, 64, 64) % 256 == 0
+    assert cb.cp_ring_attn_bwd_workspace_bytes(1, 0, 64, 64, 64) == 0
+
+
+def _ring_bwd(lib, n_steps=2, ws_bytes=None, copy_stream=ctypes.c_void_p(0x1234), stream=None, dq=None,
+              dk_override=None, workspace=None, D=128, acc=None):
+    L = 64
+    qt = cb.CpChunks.make([0, 192], L)
+    m = max(n_steps, 1)
+    tabs = [cb.cp_zigzag_chunks(2, 0, L, j % 2)[1] for j in range(m)]
+    T = cb.CpChunks * m
+    arr = lambda base: (ctypes.c_void_p * m)(*[ALIGNED + (base + j) * 1024 * MB for j in range(m)])
+    ks, vs, dks, dvs = arr(10), arr(40), arr(70), arr(100)
+    if dk_override is not None:
+        dks[1] = dk_override
+    need = cb.cp_ring_attn_bwd_workspace_bytes(1, 2, 128, 128, 128)
+    accp = None if acc is None else (ctypes.c_int * m)(*acc)
+    return lib.cp_ring_attn_bwd(fake(0), ctypes.byref(qt), fake(1), fake(2), fake(3), ks, vs, T(*tabs), n_steps,
+                                dks, dvs, accp, dq or fake(4), 1, 2, D, 0.088, workspace or fake(5),
+                                need if ws_bytes is None else ws_bytes, stream, copy_stream)
+
+
+def test_ring_bwd_validation(lib):
+    assert _ring_bwd(lib, n_steps=0) == cb.CP_ERR_INVALID
+    assert _ring_bwd(lib, n_steps=65) == cb.CP_ERR_INVALID
+    assert _ring_bwd(lib, D=96) == cb.CP_ERR_UNSUPPORTED
+    assert _ring_bwd(lib, ws_bytes=1000) == cb.CP_ERR_WORKSPACE
+    assert "needed" in cb.cp_last_error()
+    assert _ring_bwd(lib, copy_stream=None, stream=ctypes.c_void_p(0x99)) == cb.CP_ERR_INVALID
+    assert _ring_bwd(lib, workspace=ctypes.c_void_p(ALIGNED + 128)) == cb.CP_ERR_INVALID      # misaligned
+    assert _ring_bwd(lib, workspace=fake(4)) == cb.CP_ERR_INVALID                              # overlaps dq
+    assert _ring_bwd(lib, dq=fake(0)) == cb.CP_ERR_INVALID                                     # dq aliases q
+    assert _ring_bwd(lib, dk_override=ALIGNED + 70 * 1024 * MB) == cb.CP_ERR_INVALID           # two steps share dK
+    assert _ring_bwd(lib, dk_override=ALIGNED + 10 * 1024 * MB) == cb.CP_ERR_INVALID           # dK aliases K
+    assert _ring_bwd(lib, dk_override=ALIGNED + 70 * 1024 * MB + 8) == cb.CP_ERR_INVALID       # misaligned
+    assert cb.cp_last_error()

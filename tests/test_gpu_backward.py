@@ -320,3 +320,97 @@ def test_ring_backward_end_to_end(N, L, D, H):
     for i, (name, got) in enumerate((("dq", dq_full), ("dk", dk_full), ("dv", dv_full))):
         r_all = np.stack([x[i] for x in ref])[None]
         assert_grad(name, torch.from_numpy(got), r_all)
+
+
+# ---------------------------------------------------------------- ring driver
+def run_ring_bwd(q, q_tab, do, out, lse, ks, vs, kv_tabs, dks, dvs, scale, acc=None, copy_stream=None):
+    B, H, Sq, D = q.shape
+    Skv = ks[0].shape[2]
+    dq = torch.empty((B, H, Sq, D), dtype=torch.float32, device=DEV)
+    ws = torch.empty(cp.cp_ring_attn_bwd_workspace_bytes(B, H, Skv, D, Sq), dtype=torch.uint8, device=DEV)
+    cp.cp_ring_attn_bwd(q, q_tab, do, out, lse, ks, vs, kv_tabs, dks, dvs, dq, scale, ws, dkv_accumulate=acc,
+                        copy_stream=torch.cuda.Stream() if copy_stream is None else copy_stream)
+    return dq
+
+
+@pytest.mark.parametrize("N,L,D,H", [(2, 64, 64, 2), (4, 128, 128, 2), (2, 256, 128, 2)])
+def test_ring_attn_bwd_all_ranks(N, L, D, H):
+    """cp_ring_attn_bwd on every rank after the GPU forward: each block's dK/dV buffers start at zero and
+    every rank adds its contribution (all steps accumulate); the assembled gradients match the oracle's
+    full-sequence causal attention gradients."""
+    S = 2 * N * L
+    scale = 1 / math.sqrt(D)
+    Q, K, V = workloads.make_qkv_scaled((1, H, S, D), 60 + N + L)
+    gen = torch.Generator().manual_seed(61 + N + L)
+    dO = torch.randn(1, H, S, D, generator=gen).to(torch.bfloat16)
+    Skv = 2 * L
+    blocks = {src: (torch.zeros((1, H, Skv, D), dtype=torch.float32, device=DEV),
+                    torch.zeros((1, H, Skv, D), dtype=torch.float32, device=DEV)) for src in range(N)}
+    dq_full = np.zeros((1, H, S, D))
+    for r in range(N):
+        _announce("ring attn bwd", N, L, D, "rank", r)
+        q_tab, kv_tabs = zigzag_tables(N, r, L)
+        q, do = gather(Q, q_tab, DEV), gather(dO, q_tab, DEV)
+        ks = [gather(K, t, DEV) for t in kv_tabs]
+        vs = [gather(V, t, DEV) for t in kv_tabs]
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+        ws = torch.empty(cp.cp_ring_attn_workspace_bytes(1, H, Skv, D, q.shape[2]), dtype=torch.uint8, device=DEV)
+        cp.cp_ring_attn_fwd(q, q_tab, ks, vs, kv_tabs, out, lse, scale, ws, copy_stream=torch.cuda.Stream())
+        dks = [blocks[(r - j) % N][0] for j in range(N)]
+        dvs = [blocks[(r - j) % N][1] for j in range(N)]
+        dq = run_ring_bwd(q, q_tab, do, out, lse, ks, vs, kv_tabs, dks, dvs, scale, acc=[1] * N)
+        torch.cuda.synchronize()
+        dq_full[:, :, positions(q_tab)] = dq.cpu().numpy()
+    dk_full = np.zeros((1, H, S, D))
+    dv_full = np.zeros((1, H, S, D))
+    for src, (dk, dv) in blocks.items():
+        p = positions(zigzag_tables(N, src, L)[0])
+        dk_full[:, :, p] = dk.cpu().numpy()
+        dv_full[:, :, p] = dv.cpu().numpy()
+    ref = _per_head(1, H, lambda b, h: oracle.causal_attention_grad(
+        oracle.to_f64(Q[b, h]), oracle.to_f64(K[b, h]), oracle.to_f64(V[b, h]), oracle.to_f64(dO[b, h]), scale))
+    for i, (name, got) in enumerate((("dq", dq_full), ("dk", dk_full), ("dv", dv_full))):
+        r_all = np.stack([x[i] for x in ref])[None]
+        assert_grad(name, torch.from_numpy(got), r_all)
+
+
+@pytest.mark.parametrize("name,H,rank", [("s8k_cp2", 2, 1), ("s32k_cp8", 1, 0)])
+def test_ring_attn_bwd_rank_share(name, H, rank):
+    """One rank's share with the ring's own pattern (step 0 writes, later steps add to incoming partial
+    sums): dq equals the oracle's gradient of the rank's rows, dk_steps[0] this rank's contribution to its
+    own block, dk_steps[j] the incoming partial sums plus this rank's contribution.  Running every copy in
+    order on the launch stream gives identical bits."""
+    w = workloads.get(name)
+    Q, K, V = workloads.make_qkv(w, H=H)
+    dO = workloads.make_grad_out(w, H=H)
+    q_tab, kv_tabs = zigzag_tables(w.cp, rank, w.chunk_len)
+    qpos = positions(q_tab)
+    _announce("ring attn bwd share", w.describe(), "H", H, "rank", rank)
+    fwd_out, fwd_lse = forward_rows(Q, K, V, qpos, w.scale)
+    out_d, lse_d = device_inputs(fwd_out, fwd_lse)
+    q, do = gather(Q, q_tab, DEV), gather(dO, q_tab, DEV)
+    ks = [gather(K, t, DEV) for t in kv_tabs]
+    vs = [gather(V, t, DEV) for t in kv_tabs]
+    gen = torch.Generator().manual_seed(77)
+    init = [(torch.randn(ks[0].shape, generator=gen), torch.randn(ks[0].shape, generator=gen)) for _ in kv_tabs]
+    results = []
+    for in_order in (False, True):
+        dks = [a.to(DEV) for a, _ in init]
+        dvs = [b.to(DEV) for _, b in init]
+        dq = run_ring_bwd(q, q_tab, do, out_d, lse_d, ks, vs, kv_tabs, dks, dvs, w.scale,
+                          copy_stream=torch.cuda.current_stream() if in_order else None)
+        torch.cuda.synchronize()
+        results.append((dq, dks, dvs))
+    dq, dks, dvs = results[0]
+    rq_total = 0.0
+    for j, t in enumerate(kv_tabs):
+        rq, rk, rv = oracle_step_grads(Q, K, V, dO, qpos, positions(t), fwd_out, fwd_lse, w.scale)
+        rq_total = rq_total + rq
+        for nm, got, ref, x0 in (("dk", dks[j], rk, init[j][0]), ("dv", dvs[j], rv, init[j][1])):
+            mine = got.cpu().numpy().astype(np.float64) - (x0.numpy().astype(np.float64) if j > 0 else 0.0)
+            assert_grad(f"{nm}[{j}]", torch.from_numpy(mine), ref)
+    assert_grad("dq", dq, rq_total)
+    dq2, dks2, dvs2 = results[1]
+    assert torch.equal(dq, dq2)
+    assert all(torch.equal(a, b) for a, b in zip(dks + dvs, dks2 + dvs2))
