@@ -242,7 +242,9 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a) {
     sub(n & 1, 1, cur.kpos + 32);
     cur = nxt;
   }
-  store_rows<D>(a.dq + row * D, acc, a.scale, (a.accumulate & 1) != 0, g);
+  // adding a part that no key contributes to would rewrite the rows unchanged
+  const bool add_q = (a.accumulate & 1) != 0;
+  if (T > 0 || !add_q) store_rows<D>(a.dq + row * D, acc, a.scale, add_q, g);
 }
 
 // ------------------------------------------------------------ dk/dv kernel
@@ -426,6 +428,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     cur = nxt;
   }
   const bool add = (a.accumulate & 2) != 0;
+  if (T == 0 && add) return;  // no query sees these keys: the partial sums stay as they are
   store_rows<D>(a.dk + krow * D, dk, a.scale, add, g);
   store_rows<D>(a.dv + krow * D, dv, 1.f, add, g);
 }
