@@ -275,6 +275,88 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
     print(json.dumps(res), flush=True)
 
 
+def bench_allgather(args, w, Q, K, V, q, q_tab, kv_tabs, stream):
+    """All-gather form of context parallelism: one cp_attn_step_fwd of the rank's
+    queries against the keys of the whole sequence, gathered in natural order
+    (one K/V chunk of S tokens).  The visible pairs, and so the flops, are the
+    ring's.  The gather itself (the other ranks' blocks, copied in) is not in
+    the timed region; its bytes are reported.
+    """
+    import numpy as np
+    import torch
+    import oracle
+    import long_sequence_causal_cp_amd as cp
+
+    B, H, Sq, D = q.shape
+    dev = q.device
+    k_full, v_full = K.contiguous().to(dev), V.contiguous().to(dev)
+    full = cp.CpChunks.make([0], w.S)
+    o = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+
+    def step():
+        cp.cp_attn_step_fwd(q, k_full, v_full, o, lse, out, q_tab, full, w.scale, cp.CP_STEP_WRITE, stream=stream)
+
+    pairs = visible_pairs(q_tab, kv_tabs)
+    assert pairs == visible_pairs(q_tab, [full])
+    flops = 4.0 * D * B * H * pairs
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    cp.cp_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern_ms = cp.cp_profile_read(8192)
+    cp.cp_profile_enable(False)
+    avg = statistics.fmean(kern_ms)
+    achieved = flops / (avg * 1e-3) / 1e12
+    pos = oracle.local_positions(w.S, w.cp, args.rank)
+    L = w.chunk_len
+    rows = np.array([0, L - 1, L, 2 * L - 1])
+    ro, rl = oracle.causal_attention_rows(oracle.to_f64(Q[0, 0]), oracle.to_f64(K[0, 0]), oracle.to_f64(V[0, 0]),
+                                          pos[rows], w.scale)
+    eo = float(np.max(np.abs(out[0, 0, rows].float().cpu().numpy() - ro)))
+    el = float(np.max(np.abs(lse[0, 0, rows].cpu().numpy() - rl)))
+    gather_bytes = 2 * B * H * (w.S - Sq) * D * 2
+    print(f"[bench allgather] {w.describe()} rank {args.rank}: {ms_per_step:.4f} ms/step, {value:.1f} TFLOP/s; "
+          f"step kernel {avg:.4f} ms; spot check max|dout| {eo:.2e} max|dlse| {el:.2e}", file=sys.stderr, flush=True)
+    res = {
+        "metric": "causal-effective attention TFLOP/s per CP-rank share, all-gather form (gather not timed); "
+                  "% of bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic", "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": f"{w.name}: rank {args.rank} of cp={w.cp}, local queries {Sq} tokens (zigzag chunks of {L}) "
+                        f"against the gathered {w.S} keys in one step, B={B} H={H} D={D}",
+            "seq_len": w.S, "cp": w.cp, "rank": args.rank, "B": B, "H": H, "D": D,
+            "visible_pairs_per_head": pairs, "flop_per_step": flops, "wall_s_timed": round(wall, 4),
+            "gather_bytes_not_timed": gather_bytes,
+        },
+        "roofline": {
+            "kernel": "step_kernel_256<128> over one K/V chunk of the whole sequence", "bound": "mfma",
+            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "launches_per_step": 1,
+            "avg_launch_ms": round(avg, 5),
+        },
+        "cpu_baseline": None,
+        "check": {"max_abs_dout": eo, "max_abs_dlse": el},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def copy_probe(mib, reps):
     """Plain device copy of ``mib`` MiB (torch copy kernel), for counter calibration.
 
@@ -302,8 +384,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "step_kernel_s32k_cp8_traffic.json"))
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
-                    help="fwd: the ring forward (headline); bwd: the rank's backward ring steps")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "allgather"), default="fwd",
+                    help="fwd: the ring forward (headline); bwd: the rank's backward ring steps; allgather: "
+                         "the rank's queries against the gathered keys of the whole sequence in one step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB --steps times (counter calibration)")
     args = ap.parse_args()
@@ -360,6 +443,8 @@ def main():
     if args.pass_ == "bwd":
         step()
         return bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream, gather)
+    if args.pass_ == "allgather":
+        return bench_allgather(args, w, Q, K, V, q, q_tab, kv_tabs, stream)
 
     pairs = visible_pairs(q_tab, kv_tabs)
     flops = 4.0 * D * B * H * pairs

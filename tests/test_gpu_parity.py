@@ -293,6 +293,36 @@ def test_full_sequence_single_step():
     assert eo <= OUT_TOL and el <= LSE_TOL
 
 
+@pytest.mark.parametrize("name,rank,H,rows", [("s16k_cp4", 2, 4, 256), ("s32k_cp8", 0, 2, 128)])
+def test_allgather_rank_share(name, rank, H, rows):
+    """All-gather form of context parallelism: the rank's zigzag queries against the gathered keys of the
+    whole sequence (one K/V chunk in natural order) in a single step; matches the oracle and agrees with the
+    ring result within the tolerance."""
+    w = workloads.get(name)
+    _announce("all-gather", w.describe(), "H", H, "rank", rank)
+    Q, K, V = workloads.make_qkv(w, H=H)
+    q_tab, kv_tabs = zigzag_tables(w.cp, rank, w.chunk_len)
+    q = gather(Q, q_tab, DEV)
+    k, v = K.contiguous().to(DEV), V.contiguous().to(DEV)
+    full = cp.CpChunks.make([0], w.S)
+    o = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+    out = torch.empty_like(q)
+    cp.cp_attn_step_fwd(q, k, v, o, lse, out, q_tab, full, w.scale, cp.CP_STEP_WRITE)
+    ring_out, ring_lse = run_ring(Q, K, V, q_tab, kv_tabs, w.scale, DEV)
+    torch.cuda.synchronize()
+    qpos = positions(q_tab)
+    local = np.sort(np.stack([np.random.default_rng(7 + h).choice(len(qpos), rows, replace=False)
+                              for h in range(H)]), axis=1)[None]
+    local[..., 0] = 0                      # first row of the early chunk: a single visible key
+    ro, rl = oracle_rows(Q, K, V, qpos[local], w.scale)
+    eo, el = compare(out, lse, ro, rl, local)
+    print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
+    assert eo <= OUT_TOL and el <= LSE_TOL, (eo, el)
+    assert float((out.float() - ring_out.float()).abs().max()) <= 2 * OUT_TOL
+    assert float((lse - ring_lse).abs().max()) <= 2 * LSE_TOL
+
+
 # ---------------------------------------------------------------- stream ordering
 def test_ring_unchanged_by_stream_delays():
     """Delays injected on either stream, or running the copies in order on the
