@@ -333,20 +333,21 @@ def run_ring_bwd(q, q_tab, do, out, lse, ks, vs, kv_tabs, dks, dvs, scale, acc=N
     return dq
 
 
-@pytest.mark.parametrize("N,L,D,H", [(2, 64, 64, 2), (4, 128, 128, 2), (2, 256, 128, 2)])
-def test_ring_attn_bwd_all_ranks(N, L, D, H):
+@pytest.mark.parametrize("N,L,D,H,B", [(2, 64, 64, 2, 1), (4, 128, 128, 2, 1), (2, 256, 128, 2, 1),
+                                       (3, 192, 64, 3, 2), (2, 256, 128, 4, 2)])
+def test_ring_attn_bwd_all_ranks(N, L, D, H, B):
     """cp_ring_attn_bwd on every rank after the GPU forward: each block's dK/dV buffers start at zero and
     every rank adds its contribution (all steps accumulate); the assembled gradients match the oracle's
     full-sequence causal attention gradients."""
     S = 2 * N * L
     scale = 1 / math.sqrt(D)
-    Q, K, V = workloads.make_qkv_scaled((1, H, S, D), 60 + N + L)
+    Q, K, V = workloads.make_qkv_scaled((B, H, S, D), 60 + N + L)
     gen = torch.Generator().manual_seed(61 + N + L)
-    dO = torch.randn(1, H, S, D, generator=gen).to(torch.bfloat16)
+    dO = torch.randn(B, H, S, D, generator=gen).to(torch.bfloat16)
     Skv = 2 * L
-    blocks = {src: (torch.zeros((1, H, Skv, D), dtype=torch.float32, device=DEV),
-                    torch.zeros((1, H, Skv, D), dtype=torch.float32, device=DEV)) for src in range(N)}
-    dq_full = np.zeros((1, H, S, D))
+    blocks = {src: (torch.zeros((B, H, Skv, D), dtype=torch.float32, device=DEV),
+                    torch.zeros((B, H, Skv, D), dtype=torch.float32, device=DEV)) for src in range(N)}
+    dq_full = np.zeros((B, H, S, D))
     for r in range(N):
         _announce("ring attn bwd", N, L, D, "rank", r)
         q_tab, kv_tabs = zigzag_tables(N, r, L)
@@ -355,23 +356,23 @@ def test_ring_attn_bwd_all_ranks(N, L, D, H):
         vs = [gather(V, t, DEV) for t in kv_tabs]
         out = torch.empty_like(q)
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
-        ws = torch.empty(cp.cp_ring_attn_workspace_bytes(1, H, Skv, D, q.shape[2]), dtype=torch.uint8, device=DEV)
+        ws = torch.empty(cp.cp_ring_attn_workspace_bytes(B, H, Skv, D, q.shape[2]), dtype=torch.uint8, device=DEV)
         cp.cp_ring_attn_fwd(q, q_tab, ks, vs, kv_tabs, out, lse, scale, ws, copy_stream=torch.cuda.Stream())
         dks = [blocks[(r - j) % N][0] for j in range(N)]
         dvs = [blocks[(r - j) % N][1] for j in range(N)]
         dq = run_ring_bwd(q, q_tab, do, out, lse, ks, vs, kv_tabs, dks, dvs, scale, acc=[1] * N)
         torch.cuda.synchronize()
         dq_full[:, :, positions(q_tab)] = dq.cpu().numpy()
-    dk_full = np.zeros((1, H, S, D))
-    dv_full = np.zeros((1, H, S, D))
+    dk_full = np.zeros((B, H, S, D))
+    dv_full = np.zeros((B, H, S, D))
     for src, (dk, dv) in blocks.items():
         p = positions(zigzag_tables(N, src, L)[0])
         dk_full[:, :, p] = dk.cpu().numpy()
         dv_full[:, :, p] = dv.cpu().numpy()
-    ref = _per_head(1, H, lambda b, h: oracle.causal_attention_grad(
+    ref = _per_head(B, H, lambda b, h: oracle.causal_attention_grad(
         oracle.to_f64(Q[b, h]), oracle.to_f64(K[b, h]), oracle.to_f64(V[b, h]), oracle.to_f64(dO[b, h]), scale))
     for i, (name, got) in enumerate((("dq", dq_full), ("dk", dk_full), ("dv", dv_full))):
-        r_all = np.stack([x[i] for x in ref])[None]
+        r_all = np.stack([x[i] for x in ref]).reshape(B, H, S, D)
         assert_grad(name, torch.from_numpy(got), r_all)
 
 
