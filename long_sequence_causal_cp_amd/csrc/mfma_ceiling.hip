@@ -120,9 +120,9 @@ int main() {
   std::printf("device compute units: %d; published dense bf16 peak: 2516.6 TFLOP/s\n", n_cu);
   int rc = 0;
   for (int w : {1, 2, 4}) rc |= run<0>(n_cu, w, out);
-  for (int w : {2, 4}) rc |= run<4>(n_cu, w, out);
-  for (int w : {2, 4}) rc |= run<8>(n_cu, w, out);
-  for (int w : {2, 4}) rc |= run<-1>(n_cu, w, out);
+  for (int w : {1, 2, 4}) rc |= run<4>(n_cu, w, out);
+  for (int w : {1, 2, 4}) rc |= run<8>(n_cu, w, out);
+  for (int w : {1, 2, 4}) rc |= run<-1>(n_cu, w, out);
   (void)hipDeviceSynchronize();
   (void)hipFree(out);
   return rc;
