@@ -129,6 +129,21 @@ def cpu_baseline_bwd(w, rank, budget_s, Q, K, V, kv_tabs):
     }
 
 
+def bwd_traffic(workload, kernel):
+    """Calibrated HBM bytes per launch of a backward kernel, from its counter
+    summary, only if taken on this workload and on the kernel source built now."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    try:
+        from long_sequence_causal_cp_amd.prof_summary import kernel_source_sha256, sources_for
+        with open(path) as f:
+            tj = json.load(f)
+        if tj.get("workload") == workload and tj.get("kernel_source_sha256") == kernel_source_sha256(sources_for(kernel)):
+            return round(tj["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
 def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream, gather):
     """The rank's backward share: one cp_ring_attn_bwd call.
 
@@ -260,7 +275,8 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
         "roofline": {
             "kernel": f"bwd_{dom}_kernel<128>", "bound": "mfma",
             "achieved": kernels[dom]["achieved"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(kernels[dom]["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(kernels[dom]["achieved"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": bwd_traffic(w.name, f"bwd_{dom}_kernel"),
             "kernels": kernels, "kernel_ms_per_step": round(N * (dq_ms + dkdv_ms), 5),
         },
         "timing": {

@@ -25,9 +25,15 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# the step kernel's translation unit and the headers it includes
+# the translation unit of each measured kernel family and the headers it includes
 KERNEL_SOURCES = tuple(os.path.join(HERE, "csrc", f)
                        for f in ("cp_attn_kernels.hip", "cp_attn_tile.h", "cp_attn_internal.h"))
+BWD_SOURCES = tuple(os.path.join(HERE, "csrc", f)
+                    for f in ("cp_attn_bwd.hip", "cp_attn_tile.h", "cp_attn_internal.h"))
+
+
+def sources_for(kernel: str):
+    return BWD_SOURCES if kernel.startswith("bwd_") else KERNEL_SOURCES
 
 
 def kernel_source_sha256(paths=KERNEL_SOURCES) -> str:
@@ -135,6 +141,7 @@ def main(argv=None):
     q = sub.add_parser("sq")
     q.add_argument("csv")
     q.add_argument("--cmd", required=True)
+    q.add_argument("--kernel", default="step_kernel", help="substring of the kernel name")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -144,15 +151,17 @@ def main(argv=None):
     t.add_argument("--workload", required=True)
     t.add_argument("--commands", required=True, help="the rocprofv3 commands, one string")
     t.add_argument("--json-out", required=True)
+    t.add_argument("--kernel", default="step_kernel", help="substring of the kernel name")
     a = ap.parse_args(argv)
     if a.sub == "stats":
         sys.stdout.write(stats_text(a.csv, a.cmd))
         return
     if a.sub == "sq":
-        sys.stdout.write(sq_text(a.csv, a.cmd))
+        sys.stdout.write(sq_text(a.csv, a.cmd, kernel=a.kernel))
         return
-    res = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes)
-    res.update({"workload": a.workload, "kernel_source_sha256": kernel_source_sha256(), "commands": a.commands})
+    res = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, kernel=a.kernel)
+    res.update({"workload": a.workload, "kernel": a.kernel, "kernel_source_sha256": kernel_source_sha256(sources_for(a.kernel)),
+                "commands": a.commands})
     with open(a.json_out, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
