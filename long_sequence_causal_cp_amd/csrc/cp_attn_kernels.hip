@@ -438,6 +438,13 @@ template <int D>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_num_vgpr(124))) step_kernel_256(const StepArgs a) {
   step_body<D, 8>(a);
 }
+// 128-row workgroups held to the same register budget, two per CU: for grids
+// of 256-row workgroups that would leave compute units idle, and for chunk
+// lengths that are multiples of 128 but not of 256.
+template <int D>
+__global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_num_vgpr(124))) step_kernel_128(const StepArgs a) {
+  step_body<D, 4>(a);
+}
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) step_kernel_small(const StepArgs a) {
   step_body<D, NW>(a);
@@ -533,18 +540,38 @@ int step_block_rows(int q_chunk_len) {
   return (q_chunk_len % 256 == 0) ? 256 : (q_chunk_len % 128 == 0) ? 128 : 64;
 }
 
-hipError_t launch_step(const StepArgs& a, int D, hipStream_t stream) {
-  const int bm = step_block_rows(a.q_chunk_len);
+namespace {
+int device_cus() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      return cus;
+    return 256;
+  }();
+  return n;
+}
+}  // namespace
+
+hipError_t launch_step(const StepArgs& args, int D, hipStream_t stream) {
+  StepArgs a = args;
+  int bm = step_block_rows(a.q_chunk_len);
+  // Every row's result is the same whatever the row-block size (a row block
+  // only decides which tiles are staged; tiles past a row are masked to exact
+  // zeros), so the launch picks it: 256-row blocks unless their grid would
+  // leave compute units idle.
+  if (bm == 256 && (long long)a.n_order * (a.q_chunk_len / 256) * a.BH < device_cus()) bm = 128;
+  a.rb_per_chunk = a.q_chunk_len / bm;
   const long long grid = (long long)a.n_order * a.rb_per_chunk * a.BH;
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk((unsigned)(2 * bm));  // one wave per 32 rows
   if (D == 128) {
     if (bm == 256) hipLaunchKernelGGL((step_kernel_256<128>), g, blk, 0, stream, a);
-    else if (bm == 128) hipLaunchKernelGGL((step_kernel_small<128, 4>), g, blk, 0, stream, a);
+    else if (bm == 128) hipLaunchKernelGGL((step_kernel_128<128>), g, blk, 0, stream, a);
     else hipLaunchKernelGGL((step_kernel_small<128, 2>), g, blk, 0, stream, a);
   } else {
     if (bm == 256) hipLaunchKernelGGL((step_kernel_256<64>), g, blk, 0, stream, a);
-    else if (bm == 128) hipLaunchKernelGGL((step_kernel_small<64, 4>), g, blk, 0, stream, a);
+    else if (bm == 128) hipLaunchKernelGGL((step_kernel_128<64>), g, blk, 0, stream, a);
     else hipLaunchKernelGGL((step_kernel_small<64, 2>), g, blk, 0, stream, a);
   }
   return hipGetLastError();
