@@ -125,7 +125,8 @@ cp_status_t cp_attn_step_fwd(const void* q, const void* k, const void* v,
  * operand with LSE = -inf contributes nothing; both empty gives (0, -inf).
  *   o_acc, o_part fp32 [B,H,Sq,D]; lse_acc, lse_part fp32 [B,H,Sq]
  *   out_bf16_or_null: if non-NULL, also write bf16 of the merged O.
- * Supported: D a multiple of 4 (any size), Sq >= 0.
+ * Supported: D a multiple of 4 (any size), Sq >= 0 (Sq = 0 does nothing and
+ * accepts NULL pointers).
  */
 cp_status_t cp_attn_merge(float* o_acc, float* lse_acc,
                           const float* o_part, const float* lse_part,

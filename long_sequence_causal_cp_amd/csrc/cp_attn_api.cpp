@@ -323,6 +323,10 @@ cp_status_t cp_attn_merge(float* o_acc, float* lse_acc, const float* o_part, con
                           int Sq, int D, void* out_bf16_or_null, hipStream_t stream) {
   if (B < 1 || H < 1 || Sq < 0) return fail(CP_ERR_INVALID, "B, H must be >= 1 and Sq >= 0");
   if (D < 4 || D % 4 != 0) return fail(CP_ERR_INVALID, "D = %d must be a positive multiple of 4", D);
+  if (Sq == 0) {  // nothing to merge; the pointers of empty tensors may be NULL
+    g_last_error.clear();
+    return CP_OK;
+  }
   if (!o_acc || !lse_acc || !o_part || !lse_part) return fail(CP_ERR_INVALID, "NULL operand");
   if (!aligned(o_acc, 16) || !aligned(o_part, 16) || !aligned(out_bf16_or_null, 8) || !aligned(lse_acc, 4) ||
       !aligned(lse_part, 4))

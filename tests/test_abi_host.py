@@ -245,3 +245,9 @@ def test_ring_bwd_validation(lib):
     assert _ring_bwd(lib, dk_override=ALIGNED + 10 * 1024 * MB) == cb.CP_ERR_INVALID           # dK aliases K
     assert _ring_bwd(lib, dk_override=ALIGNED + 70 * 1024 * MB + 8) == cb.CP_ERR_INVALID       # misaligned
     assert cb.cp_last_error()
+
+
+def test_empty_merge_and_delta_need_no_pointers(lib):
+    # zero rows: nothing to do, NULL pointers accepted, no device call made
+    assert lib.cp_attn_merge(None, None, None, None, 1, 1, 0, 128, None, None) == cb.CP_OK
+    assert lib.cp_attn_bwd_delta(None, None, None, 1, 1, 0, 128, None) == cb.CP_OK

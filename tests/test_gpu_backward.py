@@ -334,7 +334,7 @@ def run_ring_bwd(q, q_tab, do, out, lse, ks, vs, kv_tabs, dks, dvs, scale, acc=N
 
 
 @pytest.mark.parametrize("N,L,D,H,B", [(2, 64, 64, 2, 1), (4, 128, 128, 2, 1), (2, 256, 128, 2, 1),
-                                       (3, 192, 64, 3, 2), (2, 256, 128, 4, 2)])
+                                       (3, 192, 64, 3, 2), (2, 256, 128, 4, 2), (1, 128, 128, 2, 1)])
 def test_ring_attn_bwd_all_ranks(N, L, D, H, B):
     """cp_ring_attn_bwd on every rank after the GPU forward: each block's dK/dV buffers start at zero and
     every rank adds its contribution (all steps accumulate); the assembled gradients match the oracle's

@@ -323,6 +323,25 @@ def test_allgather_rank_share(name, rank, H, rows):
     assert float((lse - ring_lse).abs().max()) <= 2 * LSE_TOL
 
 
+@pytest.mark.parametrize("N,rank", [(64, 0), (64, 63), (1, 0)])
+def test_ring_extreme_step_counts(N, rank):
+    """The most ring steps the driver takes (64, in 17 launches) and a ring of one rank (its own block, the
+    whole sequence), against the oracle on every local row."""
+    L, D, H = 64, 64, 2
+    S = 2 * N * L
+    _announce("ring extremes", "N", N, "rank", rank)
+    Q, K, V = workloads.make_qkv_scaled((1, H, S, D), 90 + N)
+    q_tab, kv_tabs = zigzag_tables(N, rank, L)
+    out, lse = run_ring(Q, K, V, q_tab, kv_tabs, 1 / math.sqrt(D), DEV)
+    torch.cuda.synchronize()
+    qpos = positions(q_tab)
+    local = np.broadcast_to(np.arange(len(qpos)), (1, H, len(qpos))).copy()
+    ro, rl = oracle_rows(Q, K, V, qpos[local], 1 / math.sqrt(D))
+    eo, el = compare(out, lse, ro, rl, local)
+    print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
+    assert eo <= OUT_TOL and el <= LSE_TOL, (eo, el)
+
+
 # ---------------------------------------------------------------- stream ordering
 def test_ring_unchanged_by_stream_delays():
     """Delays injected on either stream, or running the copies in order on the
