@@ -373,6 +373,134 @@ def bench_allgather(args, w, Q, K, V, q, q_tab, kv_tabs, stream):
     print(json.dumps(res), flush=True)
 
 
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA, twice the bf16 figure
+
+
+def bench_fp8(args, w, Q, K, V, q_tab, kv_tabs, stream):
+    """The rank's share with Q, K, V in e4m3: one cp_attn_step_fwd_fp8 per ring
+    step (step 0 writes, later steps merge, the last writes the bf16 output),
+    every step's K and transposed V resident in HBM (no staging copy).
+    Quantisation: power-of-two per-tensor scales, codes = RNE(x / scale)."""
+    import math as _m
+    import numpy as np
+    import torch
+    import oracle
+    import long_sequence_causal_cp_amd as cp
+
+    dev = torch.device("cuda:0")
+
+    def quant(x):
+        amax = float(x.abs().max())
+        sc = 2.0 ** _m.ceil(_m.log2(amax / 448.0))
+        return (x.to(torch.float64) / sc).to(torch.float32).to(torch.float8_e4m3fn), sc
+
+    (qc, sq), (kc, sk), (vc, sv) = quant(Q.float()), quant(K.float()), quant(V.float())
+
+    def g8(codes, t):
+        idx = torch.cat([torch.arange(s0, s0 + t.chunk_len) for s0 in t.starts()])
+        return codes.view(torch.uint8).index_select(2, idx).contiguous()
+
+    q = g8(qc, q_tab).to(dev).view(torch.float8_e4m3fn)
+    ks = [g8(kc, t).to(dev).view(torch.float8_e4m3fn) for t in kv_tabs]
+    vts = [g8(vc, t).transpose(2, 3).contiguous().to(dev).view(torch.float8_e4m3fn) for t in kv_tabs]
+    B, H, Sq, D = q.shape
+    N = len(kv_tabs)
+    o = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    out = torch.empty((B, H, Sq, D), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        for j in range(N):
+            cp.cp_attn_step_fwd_fp8(q, ks[j], vts[j], o, lse, out if j == N - 1 else None, q_tab, kv_tabs[j], w.scale,
+                                    sq, sk, sv, cp.CP_STEP_WRITE if j == 0 else cp.CP_STEP_MERGE, stream=stream)
+
+    pairs = visible_pairs(q_tab, kv_tabs)
+    flops = 4.0 * D * B * H * pairs
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    cp.cp_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern_ms = cp.cp_profile_read(8192)
+    cp.cp_profile_enable(False)
+    avg = statistics.fmean(kern_ms)
+    achieved = flops / N / (avg * 1e-3) / 1e12
+    # the same chain of step launches in bf16, for comparison (same box, same loop)
+    def g16(x, t):
+        idx = torch.cat([torch.arange(s0, s0 + t.chunk_len) for s0 in t.starts()])
+        return x.index_select(2, idx).contiguous().to(dev)
+    q16 = g16(Q, q_tab)
+    k16 = [g16(K, t) for t in kv_tabs]
+    v16 = [g16(V, t) for t in kv_tabs]
+    out16 = torch.empty_like(out)
+
+    def step16():
+        for j in range(N):
+            cp.cp_attn_step_fwd(q16, k16[j], v16[j], o, lse, out16 if j == N - 1 else None, q_tab, kv_tabs[j],
+                                w.scale, cp.CP_STEP_WRITE if j == 0 else cp.CP_STEP_MERGE, stream=stream)
+
+    for _ in range(args.warmup):
+        step16()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step16()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    bf16_ms = e0.elapsed_time(e1) / args.steps
+    step()
+    torch.cuda.synchronize()
+
+    pos = oracle.local_positions(w.S, w.cp, args.rank)
+    L = w.chunk_len
+    rows = np.array([0, L - 1, L, 2 * L - 1])
+    deq = lambda c, sc: c.to(torch.float64).numpy() * sc
+    kmax = int(pos[rows].max()) + 1
+    ro, rl = oracle.masked_attention(deq(qc[0, 0], sq)[pos[rows]], pos[rows], deq(kc[0, 0, :kmax], sk),
+                                     deq(vc[0, 0, :kmax], sv), np.arange(kmax), w.scale)
+    eo = float(np.max(np.abs(out[0, 0, rows].float().cpu().numpy() - ro)))
+    el = float(np.max(np.abs(lse[0, 0, rows].cpu().numpy() - rl)))
+    print(f"[bench fp8] {w.describe()} rank {args.rank}: {ms_per_step:.4f} ms/step, {value:.1f} TFLOP/s; "
+          f"fp8 step kernel {avg:.4f} ms per launch; spot check max|dout| {eo:.2e} max|dlse| {el:.2e}",
+          file=sys.stderr, flush=True)
+    res = {
+        "metric": "causal-effective attention TFLOP/s per CP-rank share, fp8 (e4m3) Q/K/V, one step launch per "
+                  "ring step; % of fp8 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3", "data": "synthetic", "pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
+        "config": {
+            "workload": f"{w.name}: rank {args.rank} of cp={w.cp}, B={B} H={H} D={D} S={w.S}, zigzag chunks of {L}, "
+                        f"{N} ring steps in fp8 (K, V^T of every step resident, no staging copy)",
+            "seq_len": w.S, "cp": w.cp, "rank": args.rank, "B": B, "H": H, "D": D,
+            "visible_pairs_per_head": pairs, "flop_per_step": flops, "wall_s_timed": round(wall, 4),
+            "scales": {"q": sq, "k": sk, "v": sv},
+            "bf16_same_chain_ms_per_step": round(bf16_ms, 5),
+        },
+        "roofline": {
+            "kernel": "fp8_step_kernel (e4m3 QK^T and PV, v_mfma_f32_32x32x16_fp8_fp8)", "bound": "mfma",
+            "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None, "launches_per_step": N,
+            "avg_launch_ms": round(avg, 5),
+        },
+        "cpu_baseline": None,
+        "check": {"max_abs_dout": eo, "max_abs_dlse": el},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def copy_probe(mib, reps):
     """Plain device copy of ``mib`` MiB (torch copy kernel), for counter calibration.
 
@@ -400,9 +528,10 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "step_kernel_s32k_cp8_traffic.json"))
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "allgather"), default="fwd",
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "allgather", "fp8"), default="fwd",
                     help="fwd: the ring forward (headline); bwd: the rank's backward ring steps; allgather: "
-                         "the rank's queries against the gathered keys of the whole sequence in one step")
+                         "the rank's queries against the gathered keys of the whole sequence in one step; fp8: "
+                         "the share's ring steps in fp8 (cp_attn_step_fwd_fp8 per step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB --steps times (counter calibration)")
     args = ap.parse_args()
@@ -461,6 +590,8 @@ def main():
         return bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream, gather)
     if args.pass_ == "allgather":
         return bench_allgather(args, w, Q, K, V, q, q_tab, kv_tabs, stream)
+    if args.pass_ == "fp8":
+        return bench_fp8(args, w, Q, K, V, q_tab, kv_tabs, stream)
 
     pairs = visible_pairs(q_tab, kv_tabs)
     flops = 4.0 * D * B * H * pairs

@@ -120,6 +120,27 @@ cp_status_t cp_attn_step_fwd(const void* q, const void* k, const void* v,
                              float softmax_scale, int mode, hipStream_t stream);
 
 /*
+ * One ring step in fp8 ([MLM] section 4: FP8 together with context
+ * parallelism): the same partial attention, fused merge and modes as
+ * cp_attn_step_fwd, with Q, K and V as e4m3 codes (OCP encoding, one byte per
+ * value) and per-tensor dequantisation factors (the values are code * scale).
+ *   q   e4m3 [B,H,Sq,D]; k  e4m3 [B,H,Skv,D]; vt  e4m3 [B,H,D,Skv] (V transposed)
+ *   o, lse, out_bf16_or_null, mode: as cp_attn_step_fwd (o row-major fp32)
+ * The scores use softmax_scale * q_scale * k_scale; the probabilities are
+ * rounded to e4m3 for the PV product (fp32 accumulation) and the output is
+ * multiplied by v_scale.
+ * Supported: D = 128, q chunk_len a multiple of 256; other shapes return
+ * CP_ERR_UNSUPPORTED.  Scales must be finite and > 0.  Errors otherwise as
+ * cp_attn_step_fwd.
+ */
+cp_status_t cp_attn_step_fwd_fp8(const void* q, const void* k, const void* vt,
+                                 float* o, float* lse, void* out_bf16_or_null,
+                                 int B, int H, int D,
+                                 const cp_chunks_t* q_chunks, const cp_chunks_t* kv_chunks,
+                                 float softmax_scale, float q_scale, float k_scale, float v_scale,
+                                 int mode, hipStream_t stream);
+
+/*
  * Standalone log-sum-exp merge of two partial results, in place on the
  * accumulator: L = ln(e^La + e^Lb), O = e^(La-L) Oa + e^(Lb-L) Ob; an
  * operand with LSE = -inf contributes nothing; both empty gives (0, -inf).
@@ -280,7 +301,7 @@ cp_status_t cp_ring_attn_bwd(const void* q, const cp_chunks_t* q_chunks,
 
 /*
  * Kernel timing for measurement.  While enabled, every attention-step kernel
- * launched by cp_attn_step_fwd / cp_ring_attn_fwd, and each of the two
+ * launched by cp_attn_step_fwd / cp_ring_attn_fwd / cp_attn_step_fwd_fp8, and each of the two
  * kernels of cp_attn_step_bwd and of every step of cp_ring_attn_bwd (dq
  * first, then dk/dv), is bracketed by two HIP
  * events on its stream.  cp_profile_read waits for those events, writes up to

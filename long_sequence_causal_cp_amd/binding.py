@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "cp_version": (i32, []),
         "cp_zigzag_chunks": (i32, [i32, i32, i32, i32, pch, pch]),
         "cp_attn_step_fwd": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, pch, pch, f32, i32, vp]),
+        "cp_attn_step_fwd_fp8": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, pch, pch, f32, f32, f32, f32, i32,
+                                       vp]),
         "cp_attn_merge": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]),
         "cp_attn_bwd_delta": (i32, [vp, vp, vp, i32, i32, i32, i32, vp]),
         "cp_attn_step_bwd": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, pch, pch, f32, i32, vp]),
@@ -158,6 +160,22 @@ def cp_attn_merge(o_acc, lse_acc, o_part, lse_part, out=None, stream=None):
     B, H, Sq, D = o_acc.shape
     _check(load_library().cp_attn_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part),
                                         B, H, Sq, D, _ptr(out), _stream(stream)))
+
+
+def cp_attn_step_fwd_fp8(q, k, vt, o, lse, out, q_chunks: CpChunks, kv_chunks: CpChunks, softmax_scale: float,
+                         q_scale: float, k_scale: float, v_scale: float, mode: int = CP_STEP_WRITE, stream=None):
+    """q, k: e4m3 [B,H,S,D]; vt: e4m3 [B,H,D,Skv] (V transposed); torch.float8_e4m3fn tensors."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        _need(t, torch.float8_e4m3fn, n)
+    _need(o, torch.float32, "o")
+    _need(lse, torch.float32, "lse")
+    _need(out, torch.bfloat16, "out")
+    B, H, _, D = q.shape
+    _check(load_library().cp_attn_step_fwd_fp8(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), _ptr(lse), _ptr(out), B, H, D,
+                                               ctypes.byref(q_chunks), ctypes.byref(kv_chunks),
+                                               float(softmax_scale), float(q_scale), float(k_scale),
+                                               float(v_scale), int(mode), _stream(stream)))
 
 
 def cp_attn_bwd_delta(out, d_out, delta, stream=None):

@@ -25,6 +25,7 @@
 
 #include "../../include/cp_attn.h"
 #include "cp_attn_internal.h"
+#include "cp_attn_fp8.h"
 
 using cpattn::StepArgs;
 
@@ -315,6 +316,78 @@ cp_status_t cp_attn_step_fwd(const void* q, const void* k, const void* v, float*
   set_order(a, active, work);
   hipError_t e = launch_step_timed(a, D, stream);
   if (e != hipSuccess) return hip_fail(e, "step kernel launch");
+  g_last_error.clear();
+  return CP_OK;
+}
+
+cp_status_t cp_attn_step_fwd_fp8(const void* q, const void* k, const void* vt, float* o, float* lse,
+                                 void* out_bf16_or_null, int B, int H, int D, const cp_chunks_t* q_chunks,
+                                 const cp_chunks_t* kv_chunks, float softmax_scale, float q_scale, float k_scale,
+                                 float v_scale, int mode, hipStream_t stream) {
+  cp_status_t st = check_common(B, H, D, softmax_scale);
+  if (st != CP_OK) return st;
+  if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
+  if ((st = check_chunks(kv_chunks, "kv_chunks")) != CP_OK) return st;
+  if (D != 128) return fail(CP_ERR_UNSUPPORTED, "fp8 step: head dim D = %d not built (128)", D);
+  if (q_chunks->chunk_len % cpattn::kFp8BlockRows != 0)
+    return fail(CP_ERR_UNSUPPORTED, "fp8 step: q chunk_len = %d must be a multiple of %d", q_chunks->chunk_len,
+                cpattn::kFp8BlockRows);
+  const float sc[3] = {q_scale, k_scale, v_scale};
+  for (float x : sc)
+    if (!std::isfinite(x) || !(x > 0.f)) return fail(CP_ERR_INVALID, "fp8 step: scales must be finite and > 0");
+  if (mode != CP_STEP_WRITE && mode != CP_STEP_MERGE) return fail(CP_ERR_INVALID, "mode = %d unknown", mode);
+  if (!q || !k || !vt || !o || !lse) return fail(CP_ERR_INVALID, "q, k, vt, o and lse must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(vt, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(out_bf16_or_null, 16))
+    return fail(CP_ERR_INVALID, "q, k, vt, o, out must be 16-byte aligned and lse 4-byte aligned");
+  const size_t BH = (size_t)B * H;
+  const size_t Sq = (size_t)q_chunks->n_chunks * q_chunks->chunk_len;
+  const size_t Skv = (size_t)kv_chunks->n_chunks * kv_chunks->chunk_len;
+  const size_t qb = BH * Sq * D, kvb = BH * Skv * D, ob = BH * Sq * D * 4, lb = BH * Sq * 4, outb = BH * Sq * D * 2;
+  const void* ins[3] = {q, k, vt};
+  const size_t insz[3] = {qb, kvb, kvb};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(ins[i], insz[i], o, ob) || overlaps(ins[i], insz[i], lse, lb) ||
+        overlaps(ins[i], insz[i], out_bf16_or_null, outb))
+      return fail(CP_ERR_INVALID, "inputs must not alias o, lse or out");
+  if (overlaps(o, ob, lse, lb) || overlaps(o, ob, out_bf16_or_null, outb) || overlaps(lse, lb, out_bf16_or_null, outb))
+    return fail(CP_ERR_INVALID, "o, lse and out must not overlap");
+
+  cpattn::Fp8StepArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint8_t*>(q);
+  a.o = o;
+  a.lse = lse;
+  a.out = static_cast<uint16_t*>(out_bf16_or_null);
+  a.BH = (int)BH;
+  a.Sq = (int)Sq;
+  a.Skv = (int)Skv;
+  a.q_chunk_len = q_chunks->chunk_len;
+  a.kv_chunk_len = kv_chunks->chunk_len;
+  a.n_kv_chunks = kv_chunks->n_chunks;
+  for (int i = 0; i < q_chunks->n_chunks; ++i) a.q_start[i] = (int)q_chunks->start[i];
+  for (int i = 0; i < kv_chunks->n_chunks; ++i) {
+    a.kc[i] = static_cast<const uint8_t*>(k) + (size_t)i * kv_chunks->chunk_len * D;
+    a.vtc[i] = static_cast<const uint8_t*>(vt) + (size_t)i * kv_chunks->chunk_len;
+    a.kv_start[i] = (int)kv_chunks->start[i];
+  }
+  a.rb_per_chunk = q_chunks->chunk_len / cpattn::kFp8BlockRows;
+  a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+  a.scale_log2 = softmax_scale * q_scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
+  std::vector<int> idx;
+  std::vector<long long> work(CP_MAX_CHUNKS, 0);
+  for (int c = 0; c < q_chunks->n_chunks; ++c) {
+    work[c] = pairs_for_chunk(q_chunks, c, kv_chunks);
+    if (mode == CP_STEP_WRITE || work[c] > 0 || out_bf16_or_null) idx.push_back(c);
+    a.flags[c] = (mode == CP_STEP_MERGE ? cpattn::kFlagMerge : 0) | cpattn::kFlagWriteO |
+                 (out_bf16_or_null ? cpattn::kFlagFinalize : 0);
+  }
+  std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return work[x] > work[y]; });
+  a.n_order = (int)idx.size();
+  for (int i = 0; i < a.n_order; ++i) a.order[i] = idx[i];
+  hipError_t e = timed(stream, [&](hipStream_t s) { return cpattn::launch_step_fp8(a, s); });
+  if (e != hipSuccess) return hip_fail(e, "fp8 step kernel launch");
   g_last_error.clear();
   return CP_OK;
 }

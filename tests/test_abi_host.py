@@ -251,3 +251,21 @@ def test_empty_merge_and_delta_need_no_pointers(lib):
     # zero rows: nothing to do, NULL pointers accepted, no device call made
     assert lib.cp_attn_merge(None, None, None, None, 1, 1, 0, 128, None, None) == cb.CP_OK
     assert lib.cp_attn_bwd_delta(None, None, None, 1, 1, 0, 128, None) == cb.CP_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), cb.CP_ERR_UNSUPPORTED),
+    (dict(qt=cb.CpChunks.make([0, 192], 64)), cb.CP_ERR_UNSUPPORTED),      # q chunks not a multiple of 256
+    (dict(vs=0.0), cb.CP_ERR_INVALID),
+    (dict(qs=float("nan")), cb.CP_ERR_INVALID),
+    (dict(mode=3), cb.CP_ERR_INVALID),
+    (dict(o=fake(0)), cb.CP_ERR_INVALID),                                   # o aliases q
+])
+def test_step_fwd_fp8_validation(lib, kw, status):
+    a = dict(D=128, qt=cb.CpChunks.make([0, 768], 256), kvt=cb.CpChunks.make([0, 768], 256), qs=0.5, ks=0.5,
+             vs=0.5, mode=0, o=None)
+    a.update(kw)
+    assert lib.cp_attn_step_fwd_fp8(fake(0), fake(1), fake(2), a["o"] or fake(3), fake(4), None, 1, 2, a["D"],
+                                    ctypes.byref(a["qt"]), ctypes.byref(a["kvt"]), 0.088, a["qs"], a["ks"],
+                                    a["vs"], a["mode"], None) == status
+    assert cb.cp_last_error()

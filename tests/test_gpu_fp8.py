@@ -1,0 +1,83 @@
+"""GPU parity of the fp8 ring step (cp_attn_step_fwd_fp8) against the fp64 oracle.
+
+Q, K and V are quantised to e4m3 with power-of-two per-tensor scales
+(tests/fp8_helpers.py); the oracle consumes exactly the dequantised values.
+A rank's share is computed as the ring's chain of steps: step 0 writes,
+later steps merge, the last one also writes the bf16 output.
+
+Tolerance: max-abs 0.1 on the output and 1e-3 on the natural-log LSE.  The
+output bound comes from the arithmetic: rounding the probabilities to e4m3
+(relative 2^-4) before the PV product, modelled in fp64 by
+fp8_helpers.emulated_error, moves the output by at most 0.035-0.039 on these
+workloads (test_fp8_error_model_within_tolerance pins that below 0.05), and
+the bf16 output adds at most 2^-9 of |out|.  The LSE is formed from fp32 sums
+of the unrounded probabilities of exact fp8 products, as in the bf16 path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import long_sequence_causal_cp_amd as cp
+from fp8_helpers import dequantize, quantize
+from gpu_helpers import positions, zigzag_tables
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+OUT_TOL_FP8 = 0.1
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    cp.load_library()
+
+
+def _gather(codes, table):
+    idx = torch.from_numpy(positions(table))
+    return codes.view(torch.uint8).index_select(2, idx).contiguous().view(torch.float8_e4m3fn)
+
+
+def _ring_fp8(qc, kc, vc, sq, sk, sv, q_tab, kv_tabs, scale):
+    q = _gather(qc, q_tab).to(DEV)
+    B, H, Sq, D = q.shape
+    o = torch.empty((B, H, Sq, D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+    out = torch.empty((B, H, Sq, D), dtype=torch.bfloat16, device=DEV)
+    for j, t in enumerate(kv_tabs):
+        k = _gather(kc, t).to(DEV)
+        vt = _gather(vc, t).view(torch.uint8).transpose(2, 3).contiguous().view(torch.float8_e4m3fn).to(DEV)
+        last = j == len(kv_tabs) - 1
+        cp.cp_attn_step_fwd_fp8(q, k, vt, o, lse, out if last else None, q_tab, t, scale, sq, sk, sv,
+                                cp.CP_STEP_WRITE if j == 0 else cp.CP_STEP_MERGE)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("name,H,ranks,rows", [("s8k_cp2", 2, (0, 1), None), ("s16k_cp4", 2, (1, 2), 256),
+                                               ("s32k_cp8", 2, (0, 7), 128)])
+def test_fp8_ring_share_matches_oracle(name, H, ranks, rows):
+    w = workloads.get(name)
+    Q, K, V = workloads.make_qkv(w, H=H)
+    (qc, sq), (kc, sk), (vc, sv) = quantize(Q.float()), quantize(K.float()), quantize(V.float())
+    Qd, Kd, Vd = (torch.from_numpy(dequantize(c, s)) for c, s in ((qc, sq), (kc, sk), (vc, sv)))
+    for r in ranks:
+        print("[case] fp8", w.describe(), "H", H, "rank", r, flush=True)
+        q_tab, kv_tabs = zigzag_tables(w.cp, r, w.chunk_len)
+        out, lse = _ring_fp8(qc, kc, vc, sq, sk, sv, q_tab, kv_tabs, w.scale)
+        qpos = positions(q_tab)
+        n = len(qpos)
+        local = np.arange(n) if rows is None else np.unique(np.concatenate(
+            [np.random.default_rng(r).choice(n, rows, replace=False), [0, 1, w.chunk_len - 1, w.chunk_len, n - 1]]))
+        eo = el = 0.0
+        for h in range(H):
+            sel = qpos[local]
+            kmax = int(sel.max()) + 1
+            ro, rl = oracle.masked_attention(Qd[0, h].numpy()[sel], sel, Kd[0, h, :kmax].numpy(),
+                                             Vd[0, h, :kmax].numpy(), np.arange(kmax), w.scale)
+            eo = max(eo, float(np.max(np.abs(out[0, h, local].float().cpu().numpy() - ro))))
+            el = max(el, float(np.max(np.abs(lse[0, h, local].cpu().numpy() - rl))))
+        print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
+        assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)

@@ -211,3 +211,4 @@ def test_backward_mutant_is_caught(kind, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             failed += 1
     assert failed >= 1, f"mutant {kind} passed every pin"
+
