@@ -255,6 +255,33 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream, hipStream_t copy_stream);
 
+/* Workspace bytes cp_ring_attn_fwd_fp8 needs: two staging slots of e4m3 K and
+ * V^T blocks (one byte per value) for up to four ring steps, plus the fp32
+ * running output [B,H,Sq,D], each rounded up to 256 bytes.  Returns 0 for
+ * non-positive sizes. */
+size_t cp_ring_attn_fwd_fp8_workspace_bytes(int B, int H, int Skv, int D, int Sq);
+
+/*
+ * A rank's whole share in fp8, replayed on one GPU: the ring of
+ * cp_ring_attn_fwd (same launch groups, staging slots, streams and events)
+ * with the steps of cp_attn_step_fwd_fp8.
+ *   q          e4m3 [B,H,Sq,D] with table *q_chunks
+ *   k_steps[j] e4m3 [B,H,Skv,D]; vt_steps[j] e4m3 [B,H,D,Skv] (V transposed)
+ *   out        bf16 [B,H,Sq,D]; lse fp32 [B,H,Sq]
+ *   scales     as cp_attn_step_fwd_fp8
+ * The staging copies move one byte per value, half of the bf16 ring's.
+ * Supported: D = 128, q chunk_len a multiple of 256.  Errors as
+ * cp_ring_attn_fwd; CP_ERR_UNSUPPORTED for other shapes.
+ */
+cp_status_t cp_ring_attn_fwd_fp8(const void* q, const cp_chunks_t* q_chunks,
+                                 const void* const* k_steps, const void* const* vt_steps,
+                                 const cp_chunks_t* kv_chunks_steps, int n_steps,
+                                 void* out, float* lse,
+                                 int B, int H, int D, float softmax_scale,
+                                 float q_scale, float k_scale, float v_scale,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, hipStream_t copy_stream);
+
 /* Workspace bytes cp_ring_attn_bwd needs: Delta fp32 [B,H,Sq], then two
  * staging slots, each for one step's K and V blocks (bf16 [B,H,Skv,D]) and
  * the dK and dV partial sums that travel with it (fp32 [B,H,Skv,D]), each

@@ -78,6 +78,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "cp_ring_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "cp_ring_attn_fwd": (i32, [vp, pch, ctypes.POINTER(vp), ctypes.POINTER(vp), pch, i32, vp, vp,
                                    i32, i32, i32, f32, vp, sz, vp, vp]),
+        "cp_ring_attn_fwd_fp8_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "cp_ring_attn_fwd_fp8": (i32, [vp, pch, ctypes.POINTER(vp), ctypes.POINTER(vp), pch, i32, vp, vp,
+                                       i32, i32, i32, f32, f32, f32, f32, vp, sz, vp, vp]),
         "cp_ring_attn_bwd_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "cp_ring_attn_bwd": (i32, [vp, pch, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), pch, i32,
                                    ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i32), vp,
@@ -227,6 +230,35 @@ def cp_ring_attn_fwd(q, q_chunks: CpChunks, k_steps, v_steps, kv_chunks_steps, o
                                            _ptr(out), _ptr(lse), B, H, D, float(softmax_scale),
                                            _ptr(workspace), workspace.numel(), _stream(stream),
                                            _stream(copy_stream)))
+
+
+def cp_ring_attn_fwd_fp8_workspace_bytes(B: int, H: int, Skv: int, D: int, Sq: int) -> int:
+    return int(load_library().cp_ring_attn_fwd_fp8_workspace_bytes(B, H, Skv, D, Sq))
+
+
+def cp_ring_attn_fwd_fp8(q, q_chunks: CpChunks, k_steps, vt_steps, kv_chunks_steps, out, lse, softmax_scale: float,
+                         q_scale: float, k_scale: float, v_scale: float, workspace, stream=None, copy_stream=None):
+    """q, k_steps: e4m3 [B,H,S,D]; vt_steps: e4m3 [B,H,D,Skv]; torch.float8_e4m3fn tensors."""
+    import torch
+    _need(q, torch.float8_e4m3fn, "q")
+    _need(out, torch.bfloat16, "out")
+    _need(lse, torch.float32, "lse")
+    _need(workspace, torch.uint8, "workspace")
+    n = len(k_steps)
+    if len(vt_steps) != n or len(kv_chunks_steps) != n:
+        raise ValueError("k_steps, vt_steps and kv_chunks_steps must have the same length")
+    for t in list(k_steps) + list(vt_steps):
+        _need(t, torch.float8_e4m3fn, "k/vt step")
+    kp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in k_steps])
+    vp_ = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in vt_steps])
+    tables = (CpChunks * max(n, 1))(*kv_chunks_steps)
+    if copy_stream is None:
+        raise ValueError("copy_stream is required (a torch.cuda.Stream; stream itself runs the copies in order)")
+    B, H, _, D = q.shape
+    _check(load_library().cp_ring_attn_fwd_fp8(_ptr(q), ctypes.byref(q_chunks), kp, vp_, tables, n, _ptr(out),
+                                               _ptr(lse), B, H, D, float(softmax_scale), float(q_scale),
+                                               float(k_scale), float(v_scale), _ptr(workspace), workspace.numel(),
+                                               _stream(stream), _stream(copy_stream)))
 
 
 def cp_ring_attn_bwd_workspace_bytes(B: int, H: int, Skv: int, D: int, Sq: int) -> int:

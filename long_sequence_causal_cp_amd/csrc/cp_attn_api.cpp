@@ -250,6 +250,131 @@ cp_status_t get_events(int n, std::vector<hipEvent_t>& out) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// ---------------- ring replay shared by the bf16 and fp8 forwards ----------------
+// One launch of a ring forward: the steps it covers, the base of each step's
+// K and V block (the caller's for step 0, a staging slot after it), the query
+// chunks it computes with their merge/finalize flags, and their work.
+struct RingLaunch {
+  int first_step = 0, count = 0;
+  const void* k[kStepsPerLaunch] = {};
+  const void* v[kStepsPerLaunch] = {};
+  std::vector<int> active;
+  int flags[CP_MAX_CHUNKS] = {};
+  std::vector<long long> work;
+};
+
+// Launches: step 0 on the caller's block, then steps 1 .. n_steps-1 in the
+// fewest groups of at most kStepsPerLaunch steps (and at most CP_MAX_CHUNKS
+// chunks), split as evenly as possible with the smaller groups first: one
+// launch attends the query block to every staged block of its group.
+// Staging is double buffered per launch: the blocks of launch g go to slot
+// g % 2 on copy_stream while launch g-1 computes, and a later group is never
+// smaller, so its copies fit under the launch before it.  `slots` holds the
+// two slots, K blocks then V blocks (kv_bytes each, 256-byte aligned);
+// `launch(rl)` enqueues the kernel of one launch on `stream`.
+template <class Launch>
+cp_status_t ring_replay(const cp_chunks_t* q_chunks, const void* const* k_steps, const void* const* v_steps,
+                        const cp_chunks_t* kv_chunks_steps, int n_steps, size_t kv_bytes, unsigned char* slots,
+                        hipStream_t stream, hipStream_t copy_stream, Launch&& launch) {
+  cp_status_t st;
+  const int nkv = kv_chunks_steps[0].n_chunks;
+  const int per = std::max(1, std::min(kStepsPerLaunch, CP_MAX_CHUNKS / nkv));  // steps per staged launch
+  std::vector<int> l_first, l_count;  // launches: first step, number of steps
+  l_first.push_back(0);
+  l_count.push_back(1);
+  {
+    const int rest = n_steps - 1;
+    const int groups = (rest + per - 1) / per;
+    for (int g = 0, j = 1; g < groups; ++g) {
+      const int cnt = rest / groups + (g >= groups - rest % groups ? 1 : 0);
+      l_first.push_back(j);
+      l_count.push_back(cnt);
+      j += cnt;
+    }
+  }
+  const int n_launch = (int)l_first.size();
+  const int nq = q_chunks->n_chunks;
+  std::vector<std::vector<long long>> work(n_launch, std::vector<long long>(CP_MAX_CHUNKS, 0));
+  std::vector<int> first(nq, -1), last(nq, -1);
+  for (int l = 0; l < n_launch; ++l)
+    for (int c = 0; c < nq; ++c) {
+      for (int j = l_first[l]; j < l_first[l] + l_count[l]; ++j)
+        work[l][c] += pairs_for_chunk(q_chunks, c, &kv_chunks_steps[j]);
+      if (work[l][c] > 0) {
+        if (first[c] < 0) first[c] = l;
+        last[c] = l;
+      }
+    }
+  for (int c = 0; c < nq; ++c)
+    if (first[c] < 0) first[c] = last[c] = n_launch - 1;  // no key at all: write O = 0, LSE = -inf
+
+  // slots, in blocks of kv_slot bytes: K slot 0 [0, P), K slot 1 [P, 2P),
+  // V slot 0 [2P, 3P), V slot 1 [3P, 4P) with P = kStepsPerLaunch (a slot's
+  // blocks adjacent)
+  const size_t kv_slot = round256(kv_bytes);
+  auto slot_k = [&](int g, int i) -> void* { return slots + (size_t)(kStepsPerLaunch * (g & 1) + i) * kv_slot; };
+  auto slot_v = [&](int g, int i) -> void* {
+    return slots + (size_t)(2 * kStepsPerLaunch + kStepsPerLaunch * (g & 1) + i) * kv_slot;
+  };
+
+  std::vector<hipEvent_t> ev;
+  if ((st = get_events(2 + 2 * n_launch, ev)) != CP_OK) return st;
+  hipEvent_t ev_entry = ev[0], ev_done = ev[1];
+  hipEvent_t* copied = &ev[2];              // per launch: its blocks are staged
+  hipEvent_t* released = &ev[2 + n_launch];  // per launch: done reading its slot
+
+  hipError_t e;
+#define HIP_TRY(call, what)                                   \
+  do {                                                        \
+    if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
+  } while (0)
+
+  // copy the blocks of staged launch l (>= 1, pair slot g = l - 1) on copy_stream
+  auto stage = [&](int l) -> cp_status_t {
+    const int g = l - 1;
+    if (g >= 2) HIP_TRY(hipStreamWaitEvent(copy_stream, released[l - 2], 0), "hipStreamWaitEvent");
+    for (int i = 0; i < l_count[l]; ++i) {
+      const int j = l_first[l] + i;
+      HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k(g, i), v_steps[j], slot_v(g, i), kv_bytes, copy_stream),
+              "staging copy launch");
+    }
+    HIP_TRY(hipEventRecord(copied[l], copy_stream), "hipEventRecord");
+    return CP_OK;
+  };
+
+  HIP_TRY(hipEventRecord(ev_entry, stream), "hipEventRecord");
+  HIP_TRY(hipStreamWaitEvent(copy_stream, ev_entry, 0), "hipStreamWaitEvent");
+  for (int l = 1; l < n_launch && l <= 2; ++l)
+    if ((st = stage(l)) != CP_OK) return st;
+  for (int l = 0; l < n_launch; ++l) {
+    if (l >= 1) HIP_TRY(hipStreamWaitEvent(stream, copied[l], 0), "hipStreamWaitEvent");
+    RingLaunch rl;
+    rl.first_step = l_first[l];
+    rl.count = l_count[l];
+    for (int i = 0; i < rl.count; ++i) {
+      rl.k[i] = (l == 0) ? k_steps[0] : slot_k(l - 1, i);
+      rl.v[i] = (l == 0) ? v_steps[0] : slot_v(l - 1, i);
+    }
+    for (int c = 0; c < nq; ++c) {
+      if (l < first[c] || l > last[c] || (work[l][c] == 0 && l != last[c] && l != first[c])) continue;
+      rl.active.push_back(c);
+      rl.flags[c] = (l == first[c] ? 0 : cpattn::kFlagMerge) |
+                    (l == last[c] ? cpattn::kFlagFinalize : cpattn::kFlagWriteO);
+    }
+    rl.work = work[l];
+    HIP_TRY(launch(rl), "step kernel launch");
+    if (l + 2 < n_launch) {
+      // launch l + 2 reuses the pair slot launch l reads
+      if (l >= 1) HIP_TRY(hipEventRecord(released[l], stream), "hipEventRecord");
+      if (l + 2 >= 3 && (st = stage(l + 2)) != CP_OK) return st;
+    }
+  }
+  HIP_TRY(hipEventRecord(ev_done, copy_stream), "hipEventRecord");
+  HIP_TRY(hipStreamWaitEvent(stream, ev_done, 0), "hipStreamWaitEvent");
+#undef HIP_TRY
+  return CP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -532,119 +657,122 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
         return fail(CP_ERR_INVALID, "out, lse and workspace must not overlap");
   }
 
-  // ---- plan ----
-  // Launches: step 0 on the caller's block, then steps 1 .. n_steps-1 in the
-  // fewest groups of at most kStepsPerLaunch steps (and at most
-  // CP_MAX_CHUNKS chunks), split as evenly as possible with the smaller
-  // groups first: one launch attends the query block to every staged block
-  // of its group.  Staging is double buffered per launch: the blocks of
-  // launch g go to slot g % 2 on copy_stream while launch g-1 computes, and
-  // a later group is never smaller, so its copies fit under the launch
-  // before it.
-  const int nkv = kv_chunks_steps[0].n_chunks;
-  const int per = std::max(1, std::min(kStepsPerLaunch, CP_MAX_CHUNKS / nkv));  // steps per staged launch
-  std::vector<int> l_first, l_count;  // launches: first step, number of steps
-  l_first.push_back(0);
-  l_count.push_back(1);
-  {
-    const int rest = n_steps - 1;
-    const int groups = (rest + per - 1) / per;
-    for (int g = 0, j = 1; g < groups; ++g) {
-      const int cnt = rest / groups + (g >= groups - rest % groups ? 1 : 0);
-      l_first.push_back(j);
-      l_count.push_back(cnt);
-      j += cnt;
-    }
-  }
-  const int n_launch = (int)l_first.size();
-  const int nq = q_chunks->n_chunks;
-  std::vector<std::vector<long long>> work(n_launch, std::vector<long long>(CP_MAX_CHUNKS, 0));
-  std::vector<int> first(nq, -1), last(nq, -1);
-  for (int l = 0; l < n_launch; ++l)
-    for (int c = 0; c < nq; ++c) {
-      for (int j = l_first[l]; j < l_first[l] + l_count[l]; ++j)
-        work[l][c] += pairs_for_chunk(q_chunks, c, &kv_chunks_steps[j]);
-      if (work[l][c] > 0) {
-        if (first[c] < 0) first[c] = l;
-        last[c] = l;
-      }
-    }
-  for (int c = 0; c < nq; ++c)
-    if (first[c] < 0) first[c] = last[c] = n_launch - 1;  // no key at all: write O = 0, LSE = -inf
-
-  // workspace, in blocks of kv_slot bytes: K slot 0 [0, P), K slot 1 [P, 2P),
-  // V slot 0 [2P, 3P), V slot 1 [3P, 4P) with P = kStepsPerLaunch (a slot's
-  // blocks adjacent), then the fp32 running O
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  const size_t kv_slot = round256(kv_bytes);
-  auto slot_k = [&](int g, int i) -> void* { return ws + (size_t)(kStepsPerLaunch * (g & 1) + i) * kv_slot; };
-  auto slot_v = [&](int g, int i) -> void* {
-    return ws + (size_t)(2 * kStepsPerLaunch + kStepsPerLaunch * (g & 1) + i) * kv_slot;
-  };
-  float* o_run = reinterpret_cast<float*>(ws + 4 * kStepsPerLaunch * kv_slot);
+  float* o_run = reinterpret_cast<float*>(ws + 4 * kStepsPerLaunch * round256(kv_bytes));
+  st = ring_replay(q_chunks, k_steps, v_steps, kv_chunks_steps, n_steps, kv_bytes, ws, stream, copy_stream,
+                   [&](const RingLaunch& rl) -> hipError_t {
+                       StepArgs a;
+                       base_args(a, q, rl.k[0], rl.v[0], o_run, lse, out, B, H, D, q_chunks,
+                                 &kv_chunks_steps[rl.first_step], softmax_scale);
+                       for (int i = 1; i < rl.count; ++i)
+                         add_kv_block(a, rl.k[i], rl.v[i], &kv_chunks_steps[rl.first_step + i]);
+                       for (int c : rl.active) a.flags[c] = rl.flags[c] | cpattn::kFlagLaneO;
+                       set_order(a, rl.active, rl.work);
+                       return launch_step_timed(a, D, stream);
+                     });
+  if (st == CP_OK) g_last_error.clear();
+  return st;
+}
 
-  std::vector<hipEvent_t> ev;
-  if ((st = get_events(2 + 2 * n_launch, ev)) != CP_OK) return st;
-  hipEvent_t ev_entry = ev[0], ev_done = ev[1];
-  hipEvent_t* copied = &ev[2];              // per launch: its blocks are staged
-  hipEvent_t* released = &ev[2 + n_launch];  // per launch: done reading its slot
+size_t cp_ring_attn_fwd_fp8_workspace_bytes(int B, int H, int Skv, int D, int Sq) {
+  if (B <= 0 || H <= 0 || Skv <= 0 || D <= 0 || Sq <= 0) return 0;
+  const size_t kv = round256((size_t)B * H * Skv * D);
+  const size_t o = round256((size_t)B * H * Sq * D * 4);
+  return 4 * kStepsPerLaunch * kv + o;
+}
 
-  hipError_t e;
-#define HIP_TRY(call, what)                 \
-  do {                                      \
-    if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
-  } while (0)
-
-  // copy the blocks of staged launch l (>= 1, pair slot g = l - 1) on copy_stream
-  auto stage = [&](int l) -> cp_status_t {
-    const int g = l - 1;
-    if (g >= 2) HIP_TRY(hipStreamWaitEvent(copy_stream, released[l - 2], 0), "hipStreamWaitEvent");
-    for (int i = 0; i < l_count[l]; ++i) {
-      const int j = l_first[l] + i;
-      HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k(g, i), v_steps[j], slot_v(g, i), kv_bytes, copy_stream),
-              "staging copy launch");
-    }
-    HIP_TRY(hipEventRecord(copied[l], copy_stream), "hipEventRecord");
-    return CP_OK;
-  };
-
-  HIP_TRY(hipEventRecord(ev_entry, stream), "hipEventRecord");
-  HIP_TRY(hipStreamWaitEvent(copy_stream, ev_entry, 0), "hipStreamWaitEvent");
-  for (int l = 1; l < n_launch && l <= 2; ++l)
-    if ((st = stage(l)) != CP_OK) return st;
-  for (int l = 0; l < n_launch; ++l) {
-    if (l >= 1) HIP_TRY(hipStreamWaitEvent(stream, copied[l], 0), "hipStreamWaitEvent");
-    StepArgs a;
-    const int j0 = l_first[l];
-    if (l == 0) {
-      base_args(a, q, k_steps[0], v_steps[0], o_run, lse, out, B, H, D, q_chunks, &kv_chunks_steps[0],
-                softmax_scale);
-    } else {
-      base_args(a, q, slot_k(l - 1, 0), slot_v(l - 1, 0), o_run, lse, out, B, H, D, q_chunks,
-                &kv_chunks_steps[j0], softmax_scale);
-      for (int i = 1; i < l_count[l]; ++i)
-        add_kv_block(a, slot_k(l - 1, i), slot_v(l - 1, i), &kv_chunks_steps[j0 + i]);
-    }
-    std::vector<int> active;
-    for (int c = 0; c < nq; ++c) {
-      if (l < first[c] || l > last[c] || (work[l][c] == 0 && l != last[c] && l != first[c])) continue;
-      active.push_back(c);
-      a.flags[c] = (l == first[c] ? 0 : cpattn::kFlagMerge) |
-                   (l == last[c] ? cpattn::kFlagFinalize : cpattn::kFlagWriteO) | cpattn::kFlagLaneO;
-    }
-    set_order(a, active, work[l]);
-    HIP_TRY(launch_step_timed(a, D, stream), "step kernel launch");
-    if (l + 2 < n_launch) {
-      // launch l + 2 reuses the pair slot launch l reads
-      if (l >= 1) HIP_TRY(hipEventRecord(released[l], stream), "hipEventRecord");
-      if (l + 2 >= 3 && (st = stage(l + 2)) != CP_OK) return st;
-    }
+cp_status_t cp_ring_attn_fwd_fp8(const void* q, const cp_chunks_t* q_chunks, const void* const* k_steps,
+                                 const void* const* vt_steps, const cp_chunks_t* kv_chunks_steps, int n_steps,
+                                 void* out, float* lse, int B, int H, int D, float softmax_scale, float q_scale,
+                                 float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, hipStream_t copy_stream) {
+  cp_status_t st = check_common(B, H, D, softmax_scale);
+  if (st != CP_OK) return st;
+  if (D != 128) return fail(CP_ERR_UNSUPPORTED, "fp8 ring: head dim D = %d not built (128)", D);
+  if (n_steps < 1 || n_steps > CP_MAX_STEPS)
+    return fail(CP_ERR_INVALID, "n_steps = %d outside [1, %d]", n_steps, CP_MAX_STEPS);
+  if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
+  if (q_chunks->chunk_len % cpattn::kFp8BlockRows != 0)
+    return fail(CP_ERR_UNSUPPORTED, "fp8 ring: q chunk_len = %d must be a multiple of %d", q_chunks->chunk_len,
+                cpattn::kFp8BlockRows);
+  const float sc[3] = {q_scale, k_scale, v_scale};
+  for (float x : sc)
+    if (!std::isfinite(x) || !(x > 0.f)) return fail(CP_ERR_INVALID, "fp8 ring: scales must be finite and > 0");
+  if (!k_steps || !vt_steps || !kv_chunks_steps) return fail(CP_ERR_INVALID, "k_steps, vt_steps, kv_chunks_steps NULL");
+  for (int j = 0; j < n_steps; ++j) {
+    char name[48];
+    snprintf(name, sizeof(name), "kv_chunks_steps[%d]", j);
+    if ((st = check_chunks(&kv_chunks_steps[j], name)) != CP_OK) return st;
+    if (kv_chunks_steps[j].n_chunks != kv_chunks_steps[0].n_chunks ||
+        kv_chunks_steps[j].chunk_len != kv_chunks_steps[0].chunk_len)
+      return fail(CP_ERR_INVALID, "every step's K/V table must have the same n_chunks and chunk_len");
+    if (!k_steps[j] || !vt_steps[j] || !aligned(k_steps[j], 16) || !aligned(vt_steps[j], 16))
+      return fail(CP_ERR_INVALID, "k_steps[%d] / vt_steps[%d] NULL or not 16-byte aligned", j, j);
   }
-  HIP_TRY(hipEventRecord(ev_done, copy_stream), "hipEventRecord");
-  HIP_TRY(hipStreamWaitEvent(stream, ev_done, 0), "hipStreamWaitEvent");
-#undef HIP_TRY
-  g_last_error.clear();
-  return CP_OK;
+  if (!q || !out || !lse) return fail(CP_ERR_INVALID, "q, out and lse must be non-NULL");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return fail(CP_ERR_INVALID, "q, out must be 16-byte aligned and lse 4-byte aligned");
+  if (!workspace || !aligned(workspace, 256)) return fail(CP_ERR_INVALID, "workspace NULL or not 256-byte aligned");
+  if (!copy_stream && stream)
+    return fail(CP_ERR_INVALID, "copy_stream is NULL (pass stream itself to run the copies in order)");
+  const int Sq = q_chunks->n_chunks * q_chunks->chunk_len;
+  const int Skv = kv_chunks_steps[0].n_chunks * kv_chunks_steps[0].chunk_len;
+  const size_t need = cp_ring_attn_fwd_fp8_workspace_bytes(B, H, Skv, D, Sq);
+  if (workspace_bytes < need)
+    return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t BH = (size_t)B * H;
+  const size_t kv_bytes = BH * Skv * D, q_bytes = BH * Sq * D, out_bytes = BH * Sq * D * 2, lse_bytes = BH * Sq * 4;
+  const void* outs[3] = {workspace, out, lse};
+  const size_t outsz[3] = {need, out_bytes, lse_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(q, q_bytes, outs[i], outsz[i])) return fail(CP_ERR_INVALID, "q overlaps an output or the workspace");
+    for (int j = 0; j < n_steps; ++j)
+      if (overlaps(k_steps[j], kv_bytes, outs[i], outsz[i]) || overlaps(vt_steps[j], kv_bytes, outs[i], outsz[i]))
+        return fail(CP_ERR_INVALID, "K/V of step %d overlaps an output or the workspace", j);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j]))
+        return fail(CP_ERR_INVALID, "out, lse and workspace must not overlap");
+  }
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* o_run = reinterpret_cast<float*>(ws + 4 * kStepsPerLaunch * round256(kv_bytes));
+  st = ring_replay(q_chunks, k_steps, vt_steps, kv_chunks_steps, n_steps, kv_bytes, ws, stream, copy_stream,
+                   [&](const RingLaunch& rl) -> hipError_t {
+                     cpattn::Fp8StepArgs a;
+                     std::memset(&a, 0, sizeof(a));
+                     a.q = static_cast<const uint8_t*>(q);
+                     a.o = o_run;
+                     a.lse = lse;
+                     a.out = static_cast<uint16_t*>(out);
+                     a.BH = (int)BH;
+                     a.Sq = Sq;
+                     a.Skv = Skv;
+                     a.q_chunk_len = q_chunks->chunk_len;
+                     a.kv_chunk_len = kv_chunks_steps[0].chunk_len;
+                     for (int i = 0; i < q_chunks->n_chunks; ++i) a.q_start[i] = (int)q_chunks->start[i];
+                     for (int i = 0; i < rl.count; ++i) {
+                       const cp_chunks_t& t = kv_chunks_steps[rl.first_step + i];
+                       for (int c = 0; c < t.n_chunks; ++c, ++a.n_kv_chunks) {
+                         a.kc[a.n_kv_chunks] = static_cast<const uint8_t*>(rl.k[i]) + (size_t)c * t.chunk_len * D;
+                         a.vtc[a.n_kv_chunks] = static_cast<const uint8_t*>(rl.v[i]) + (size_t)c * t.chunk_len;
+                         a.kv_start[a.n_kv_chunks] = (int)t.start[c];
+                       }
+                     }
+                     a.rb_per_chunk = q_chunks->chunk_len / cpattn::kFp8BlockRows;
+                     a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+                     a.scale_log2 = softmax_scale * q_scale * k_scale * 1.4426950408889634f;
+                     a.v_scale = v_scale;
+                     std::vector<int> idx(rl.active);
+                     std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return rl.work[x] > rl.work[y]; });
+                     a.n_order = (int)idx.size();
+                     for (int i = 0; i < a.n_order; ++i) {
+                       a.order[i] = idx[i];
+                       a.flags[idx[i]] = rl.flags[idx[i]];
+                     }
+                     return timed(stream, [&](hipStream_t s) { return cpattn::launch_step_fp8(a, s); });
+                   });
+  if (st == CP_OK) g_last_error.clear();
+  return st;
 }
 
 size_t cp_ring_attn_bwd_workspace_bytes(int B, int H, int Skv, int D, int Sq) {

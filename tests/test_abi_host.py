@@ -269,3 +269,23 @@ def test_step_fwd_fp8_validation(lib, kw, status):
                                     ctypes.byref(a["qt"]), ctypes.byref(a["kvt"]), 0.088, a["qs"], a["ks"],
                                     a["vs"], a["mode"], None) == status
     assert cb.cp_last_error()
+
+
+def test_ring_fwd_fp8_validation(lib):
+    L = 256
+    qt = cb.CpChunks.make([0, 3 * L], L)
+    tabs = [cb.cp_zigzag_chunks(2, 0, L, j)[1] for j in range(2)]
+    T = cb.CpChunks * 2
+    ks = (ctypes.c_void_p * 2)(*[ALIGNED + (10 + j) * 1024 * MB for j in range(2)])
+    vs = (ctypes.c_void_p * 2)(*[ALIGNED + (40 + j) * 1024 * MB for j in range(2)])
+    need = cb.cp_ring_attn_fwd_fp8_workspace_bytes(1, 2, 2 * L, 128, 2 * L)
+    assert need == 16 * 2 * 2 * L * 128 + 2 * 2 * L * 128 * 4
+
+    def call(D=128, ws=need, q_tab=qt, vscale=0.5):
+        return lib.cp_ring_attn_fwd_fp8(fake(0), ctypes.byref(q_tab), ks, vs, T(*tabs), 2, fake(1), fake(2), 1, 2, D,
+                                        0.088, 0.5, 0.5, vscale, fake(3), ws, None, ctypes.c_void_p(0x1234))
+    assert call(D=64) == cb.CP_ERR_UNSUPPORTED
+    assert call(q_tab=cb.CpChunks.make([0, 192], 64)) == cb.CP_ERR_UNSUPPORTED
+    assert call(ws=need - 1) == cb.CP_ERR_WORKSPACE
+    assert call(vscale=-1.0) == cb.CP_ERR_INVALID
+    assert cb.cp_last_error()

@@ -81,3 +81,47 @@ def test_fp8_ring_share_matches_oracle(name, H, ranks, rows):
             el = max(el, float(np.max(np.abs(lse[0, h, local].cpu().numpy() - rl))))
         print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
         assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)
+
+
+@pytest.mark.parametrize("name,H,ranks,rows", [("s8k_cp2", 2, (0, 1), None), ("s32k_cp8", 2, (0, 7), 128)])
+def test_fp8_ring_driver_matches_oracle(name, H, ranks, rows):
+    """cp_ring_attn_fwd_fp8 (grouped launches, e4m3 staging copies on a side stream) against the oracle;
+    the copies run in order on the launch stream give identical bits."""
+    w = workloads.get(name)
+    Q, K, V = workloads.make_qkv(w, H=H)
+    (qc, sq), (kc, sk), (vc, sv) = quantize(Q.float()), quantize(K.float()), quantize(V.float())
+    Qd, Kd, Vd = (torch.from_numpy(dequantize(c, s)) for c, s in ((qc, sq), (kc, sk), (vc, sv)))
+    for r in ranks:
+        print("[case] fp8 ring", w.describe(), "H", H, "rank", r, flush=True)
+        q_tab, kv_tabs = zigzag_tables(w.cp, r, w.chunk_len)
+        q = _gather(qc, q_tab).to(DEV)
+        ks = [_gather(kc, t).to(DEV) for t in kv_tabs]
+        vts = [_gather(vc, t).view(torch.uint8).transpose(2, 3).contiguous().view(torch.float8_e4m3fn).to(DEV)
+               for t in kv_tabs]
+        B, _, Sq, D = q.shape
+        ws = torch.empty(cp.cp_ring_attn_fwd_fp8_workspace_bytes(B, H, ks[0].shape[2], D, Sq), dtype=torch.uint8,
+                         device=DEV)
+        res = []
+        for in_order in (False, True):
+            out = torch.empty((B, H, Sq, D), dtype=torch.bfloat16, device=DEV)
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+            cs = torch.cuda.current_stream() if in_order else torch.cuda.Stream()
+            cp.cp_ring_attn_fwd_fp8(q, q_tab, ks, vts, kv_tabs, out, lse, w.scale, sq, sk, sv, ws, copy_stream=cs)
+            torch.cuda.synchronize()
+            res.append((out, lse))
+        assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+        out, lse = res[0]
+        qpos = positions(q_tab)
+        n = len(qpos)
+        local = np.arange(n) if rows is None else np.unique(np.concatenate(
+            [np.random.default_rng(r).choice(n, rows, replace=False), [0, 1, w.chunk_len - 1, w.chunk_len, n - 1]]))
+        eo = el = 0.0
+        for h in range(H):
+            sel = qpos[local]
+            kmax = int(sel.max()) + 1
+            ro, rl = oracle.masked_attention(Qd[0, h].numpy()[sel], sel, Kd[0, h, :kmax].numpy(),
+                                             Vd[0, h, :kmax].numpy(), np.arange(kmax), w.scale)
+            eo = max(eo, float(np.max(np.abs(out[0, h, local].float().cpu().numpy() - ro))))
+            el = max(el, float(np.max(np.abs(lse[0, h, local].cpu().numpy() - rl))))
+        print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
+        assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)
