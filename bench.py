@@ -526,7 +526,7 @@ def bench_fp8(args, w, Q, K, V, q_tab, kv_tabs, stream):
             "bf16_step_chain_ms_per_step": round(bf16_ms, 5),
         },
         "roofline": {
-            "kernel": "fp8_step_kernel (e4m3 QK^T and PV, v_mfma_f32_32x32x16_fp8_fp8)", "bound": "mfma",
+            "kernel": "fp8_step_kernel (e4m3 QK^T and PV, v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales)", "bound": "mfma",
             "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None, "launches_per_step": n_launch,
             "avg_launch_ms": round(avg, 5),

@@ -13,22 +13,31 @@
 //
 // Values: Q, K, V hold e4m3 codes with per-tensor dequantisation factors;
 // q_scale * k_scale is folded into the softmax scale and v_scale into the
-// output.  Products use v_mfma_f32_32x32x16_fp8_fp8 (eight codes per lane, in
-// the lane layout of the bf16 32x32x16 product) with fp32 accumulation.
+// output.  Products use gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// block scales (twice the rate of the 32x32x16 fp8 product) and fp32
+// accumulation.  Lane l holds row l % 32 of either operand and its k-indices
+// 32 (l / 32) .. + 31, 32 codes in eight dwords.
 //
-// Per 32-key sub-tile a wave forms S^T = K Q^T (one query per lane pair, as in
-// the bf16 kernel), the exponentials against the lazily kept row maximum
-// (every accepted p <= 2^8, inside e4m3's range of 448), packs P to e4m3, and
-// adds O^T += V^T P^T.  The score layout gives lane (query, half g) the keys
-// {4g..4g+3, 8+4g..8+4g+3} of each 16-key step; one v_permlane32_swap per
-// step hands the partner lane's group across, so that the P operand holds
-// keys 8g..8g+7 and V^T is read along its rows in natural key order.
+// Per 64-key tile a wave forms S^T = K Q^T for its 32 queries (two 32x32
+// accumulators, keys 0-31 and 32-63), the exponentials against the lazily
+// kept row maximum (every accepted p <= 2^8, inside e4m3's range of 448),
+// packs P to e4m3 and adds O^T += V^T P^T, k = the tile's 64 keys.  The
+// score layout gives lane (query, half g) the keys 8i + 4g + {0..3} of each
+// 32-key half; one v_permlane32_swap per i hands the partner's group across,
+// so that half 0 holds keys 0-31 and half 1 keys 32-63 in natural order, as
+// the PV product takes them.
+//
+// Software pipeline: while a wave exponentiates tile u, its MFMAs are
+// S(u+1) and O += V(u-1) P(u-1).  When a tile's row maximum rises past the
+// lazy bound (rare after the first tile), its scores are formed again from
+// K(u), which stays resident in one of three K buffers for that purpose, so
+// that S(u) need not stay live across the exponentials.
 //
 // LDS: a K tile is 64 keys x 128 bytes, its 16-byte chunk c of row r stored
 // at chunk c ^ ((r >> 1) & 7); a V^T tile is 128 rows (d) x 64 bytes (keys),
 // chunk c of row d at c ^ ((d >> 2) & 3).  Both are filled by direct-to-LDS
-// 16-byte loads, one instruction per wave per tile, and read with 8-byte
-// loads at most two lanes to a bank.
+// 16-byte loads, one instruction per wave per tile, and read with 16-byte
+// loads that touch every bank once per 16 lanes.
 #include "cp_attn_fp8.h"
 #include "cp_attn_tile.h"
 
@@ -37,7 +46,6 @@
 namespace cpattn {
 namespace {
 
-typedef unsigned long long u64;
 
 constexpr int kD8 = 128;          // head dimension of the fp8 kernel
 constexpr int kNW8 = 8;           // waves per workgroup, 32 rows each
@@ -53,28 +61,18 @@ __device__ __forceinline__ float half_sum8(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// P^T operand of one 16-key step from the 8 probabilities p[0..7] of that
-// step (keys 4g + {0..3} then 8 + 4g + {0..3}), packed to e4m3.
-__device__ __forceinline__ u64 pack_p(float p0, float p1, float p2, float p3, float p4, float p5, float p6,
-                                      float p7) {
-  int x0 = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-  x0 = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x0, true);
-  int x1 = __builtin_amdgcn_cvt_pk_fp8_f32(p4, p5, 0, false);
-  x1 = __builtin_amdgcn_cvt_pk_fp8_f32(p6, p7, x1, true);
-  // upper half-wave of x0 <-> lower half-wave of x1
-  auto r = __builtin_amdgcn_permlane32_swap((unsigned)x0, (unsigned)x1, false, false);
-  return (u64)r[0] | ((u64)r[1] << 32);
-}
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
   constexpr int D = kD8;
   constexpr int NW = kNW8;
   constexpr int BM = 32 * NW;
-  constexpr int NS = D / 16;
-  constexpr int NDB = D / 32;
+  constexpr int NK = D / 64;   // k-steps of the QK^T product
+  constexpr int NDB = D / 32;  // 32-row blocks of O^T
   constexpr int TB = kTB8;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k2[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[TB];
 
@@ -154,12 +152,12 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
   auto load_k = [&](const Cursor& t, unsigned char* buf) { global_to_lds_16(t.kp, k_ld, buf + 1024 * wave_u); };
   auto load_v = [&](const Cursor& t, unsigned char* buf) { global_to_lds_16(t.vp, v_ld, buf + 1024 * wave_u); };
 
-  // Q^T fragments: lane holds Q[row lq][16 s + 8 g .. + 8]
-  u64 qf[NS];
+  // Q^T fragments: lane holds Q[row lq][64 ks + 32 g .. + 32]
+  i32x8 qreg[NK];
   {
-    const uint8_t* qrow = a.q + (bh_q + qw_local + lq) * D + 8 * g;
+    const uint8_t* qrow = a.q + (bh_q + qw_local + lq) * D + 32 * g;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const u64*>(qrow + 16 * s);
+    for (int ks = 0; ks < NK; ++ks) qreg[ks] = *reinterpret_cast<const i32x8*>(qrow + 64 * ks);
   }
   f32x16 oacc[NDB];
 #pragma unroll
@@ -167,105 +165,135 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
   float m_run = neg_inf();
   float l_lane = 0.f;
 
-  // per-lane LDS read offsets: K rows (key lq of a sub-tile, d 16 st + 8 g),
-  // V^T rows (d 32 db + lq, keys 32 h + 16 t + 8 g)
-  int kro[NS];
+  // LDS read offsets: K row (32 j + lq), bytes 64 ks + 32 g + 16 h; V^T row
+  // (32 db + lq), bytes (keys) 32 g + 16 h
+  int kro[NK][2], vro[2];
   {
-    const int kx = (lq >> 1) & 7;
+    const int kx = (lq >> 1) & 7, vx = (lq >> 2) & 3;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) kro[st] = lq * D + 8 * g + 16 * (st ^ kx);
+    for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) kro[ks][h] = lq * D + 16 * ((4 * ks + 2 * g + h) ^ kx);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vro[h] = lq * kTileKeys + 16 * ((2 * g + h) ^ vx);
   }
-  int vro[4];
-  {
-    const int vx = (lq >> 2) & 3;
+  auto kfrag = [&](const unsigned char* kb, int j, int ks) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + kro[ks][0] + j * 32 * D);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + kro[ks][1] + j * 32 * D);
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto qfrag = [&](int ks) { return qreg[ks]; };
+  auto vfrag = [&](const unsigned char* vb, int db) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(vb + vro[0] + db * 32 * kTileKeys);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(vb + vro[1] + db * 32 * kTileKeys);
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // operand formats 0 (e4m3) for both, block scales 127 (2^0 in E8M0)
+  auto mm = [](const i32x8& x, const i32x8& y, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 127, 0, 127);
+  };
+  using SS = f32x16[2];
+  auto qk = [&](const unsigned char* kb, SS& s) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) vro[ht] = lq * kTileKeys + 8 * g + 16 * (ht ^ vx);
-  }
-
-  auto kread = [&](const unsigned char* kb, int h, int st) {
-    return *reinterpret_cast<const u64*>(kb + kro[st] + h * 32 * D);
+    for (int ks = 0; ks < NK; ++ks) {
+      const i32x8 qf = qfrag(ks);
+      s[0] = mm(kfrag(kb, 0, ks), qf, s[0]);
+      s[1] = mm(kfrag(kb, 1, ks), qf, s[1]);
+    }
   };
-  auto vread = [&](const unsigned char* vb, int h, int t, int db) {
-    return *reinterpret_cast<const u64*>(vb + vro[2 * h + t] + db * 32 * kTileKeys);
-  };
-  auto qk_sub = [&](const unsigned char* kb, int h) {
-    f32x16 s = {};
-#pragma unroll
-    for (int st = 0; st < NS; ++st) s = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)kread(kb, h, st), (long)qf[st], s, 0, 0, 0);
-    return s;
-  };
-  auto exps = [&](const f32x16& s_cur, u64 (&p_cur)[2], float negm) {
-    float e[16];
+  // exponentials of the tile's 64 keys against -negm, their lane sum, and
+  // the P^T operand (half g: keys 32 g + 0..31)
+  auto exps = [&](const SS& s, i32x8& p, float negm) {
     float lsum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], a.scale_log2, negm));
-      lsum += e[r];
+    for (int i = 0; i < 4; ++i) {
+      float e0[4], e1[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][4 * i + r], a.scale_log2, negm));
+        e1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][4 * i + r], a.scale_log2, negm));
+        lsum += e0[r] + e1[r];
+      }
+      int x0 = __builtin_amdgcn_cvt_pk_fp8_f32(e0[0], e0[1], 0, false);
+      x0 = __builtin_amdgcn_cvt_pk_fp8_f32(e0[2], e0[3], x0, true);
+      int x1 = __builtin_amdgcn_cvt_pk_fp8_f32(e1[0], e1[1], 0, false);
+      x1 = __builtin_amdgcn_cvt_pk_fp8_f32(e1[2], e1[3], x1, true);
+      auto r = __builtin_amdgcn_permlane32_swap((unsigned)x0, (unsigned)x1, false, false);
+      p[2 * i] = (int)r[0];
+      p[2 * i + 1] = (int)r[1];
     }
-    p_cur[0] = pack_p(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-    p_cur[1] = pack_p(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
     return lsum;
   };
-  auto body = [&](const f32x16& s_cur, f32x16& s_nxt, u64 (&p_cur)[2], const u64 (&p_prev)[2],
-                  const unsigned char* kn, int hn, const unsigned char* vp, int hp, float& lsum, auto exp_tag,
-                  auto qk_tag, auto pv_tag) {
+  auto body = [&](const SS& s_cur, SS& s_nxt, i32x8& p_cur, const i32x8& p_prev, const unsigned char* kn,
+                  const unsigned char* vp, float& lsum, auto exp_tag, auto qk_tag, auto pv_tag) {
     constexpr bool kExp = decltype(exp_tag)::value;
     constexpr bool kQK = decltype(qk_tag)::value;
     constexpr bool kPV = decltype(pv_tag)::value;
-    if constexpr (kQK) s_nxt = f32x16{};
+    if constexpr (kQK) {
+      s_nxt[0] = f32x16{};
+      s_nxt[1] = f32x16{};
+    }
+    i32x8 qf;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if constexpr (kQK)
-        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)kread(kn, hn, i), (long)qf[i], s_nxt, 0, 0, 0);
-      if constexpr (kPV) {
-        if (i < 2 * NDB) {
-          const int t = i / NDB, db = i % NDB;
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)vread(vp, hp, t, db), (long)p_prev[t],
-                                                                 oacc[db], 0, 0, 0);
-        }
+    for (int i = 0; i < NDB; ++i) {
+      if constexpr (kQK) {
+        const int j = i & 1, ks = i >> 1;
+        if (j == 0) qf = qfrag(ks);
+        s_nxt[j] = mm(kfrag(kn, j, ks), qf, s_nxt[j]);
       }
+      if constexpr (kPV) oacc[i] = mm(vfrag(vp, i), p_prev, oacc[i]);
     }
     if constexpr (!kExp) return false;
     lsum = exps(s_cur, p_cur, -m_run);
-    asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]));
-    constexpr int kMfma = (kQK ? NS : 0) + (kPV ? 2 * NDB : 0);
+    asm volatile("" ::"v"(p_cur));
+    constexpr int kMfma = (kQK ? 2 * NK : 0) + (kPV ? NDB : 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int i = 0; i < kMfma; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     }
     return !(lsum <= kSumLimit8);
   };
-  auto mask = [&](f32x16& s, int kpos) {
+  auto mask = [&](SS& s, int kpos) {
     const int qpos = qw_pos + lq;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kp = kpos + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (kp > qpos) s[r] = neg_inf();
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kp = kpos + 32 * j + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (kp > qpos) s[j][r] = neg_inf();
+      }
   };
-  auto sub = [&](int kpos, f32x16& s_cur, f32x16& s_nxt, u64 (&p_cur)[2], const u64 (&p_prev)[2],
-                 const unsigned char* kn, int hn, const unsigned char* vp, int hp, auto exp_tag, auto qk_tag,
-                 auto pv_tag) {
+  auto sub = [&](int kpos, SS& s_cur, SS& s_nxt, i32x8& p_cur, const i32x8& p_prev, const unsigned char* kc,
+                 const unsigned char* kn, const unsigned char* vp, auto exp_tag, auto qk_tag, auto pv_tag) {
     constexpr bool kExp = decltype(exp_tag)::value;
+    const bool diag = kpos + 63 > qw_pos;
     if constexpr (kExp) {
-      if (kpos + 31 > qw_pos) mask(s_cur, kpos);
+      if (diag) mask(s_cur, kpos);
     }
     float lsum = 0.f;
-    const bool redo = body(s_cur, s_nxt, p_cur, p_prev, kn, hn, vp, hp, lsum, exp_tag, qk_tag, pv_tag);
+    const bool redo = body(s_cur, s_nxt, p_cur, p_prev, kn, vp, lsum, exp_tag, qk_tag, pv_tag);
     if constexpr (kExp) {
       float alpha = 1.f;
       if (__any(redo)) {
+        // the scores of tile u again (K(u) stays resident until the next sub-iteration)
+        SS s;
+        qk(kc, s);
+        if (diag) mask(s, kpos);
         float mx = neg_inf();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
         mx = half_max8(mx) * a.scale_log2;
         const float m_new = fmaxf(m_run, mx);
         alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
-        lsum = exps(s_cur, p_cur, (m_run == neg_inf()) ? 0.f : -m_run);
+        lsum = exps(s, p_cur, (m_run == neg_inf()) ? 0.f : -m_run);
         if (__any(alpha != 1.f)) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
@@ -276,55 +304,82 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
       l_lane = __builtin_fmaf(l_lane, alpha, lsum);
     }
   };
-  Cursor tm = chunk_after(-1);
-  Cursor tv = next_tile(tm);
-  Cursor tk = next_tile(tv);
-  auto barrier_and_prefetch = [&](int n, unsigned char* k_dst, unsigned char* v_dst) {
+  // Tile u: K(u) in one of three K buffers (kb_c; kb_n holds K(u+1), kb_f
+  // receives K(u+2)), V(u) in V buffer u & 1.  Sub-iteration u forms P(u)
+  // while its MFMAs are S(u+1) and O += V(u-1) P(u-1); K(u) stays resident
+  // through it, for the rare recomputation of S(u).  At its top every wave is
+  // done with K(u-1) and V(u-2); K(u+1) and V(u-1) have landed; load K(u+2)
+  // and V(u) into those buffers.
+  Cursor tc = chunk_after(-1);  // tile u
+  Cursor tn = next_tile(tc);    // tile u+1
+  Cursor tnn = next_tile(tn);   // tile u+2
+  unsigned char* kb_c = lds_k0;
+  unsigned char* kb_n = lds_k1;
+  unsigned char* kb_f = lds_k2;
+  auto barrier_and_prefetch = [&](int u) {
     wait_vmem_all();
     __syncthreads();
-    if (n + 2 < T) load_k(tk, k_dst);
-    if (n + 1 < T) load_v(tv, v_dst);
+    if (u + 2 < T) load_k(tnn, kb_f);
+    if (u >= 1) load_v(tc, (u & 1) ? lds_v1 : lds_v0);
   };
   auto advance = [&]() {
-    tm = tv;
-    tv = tk;
-    tk = next_tile(tk);
+    tc = tn;
+    tn = tnn;
+    tnn = next_tile(tnn);
+    unsigned char* const t = kb_c;
+    kb_c = kb_n;
+    kb_n = kb_f;
+    kb_f = t;
   };
   using Yes = std::true_type;
   using No = std::false_type;
   if (T > 0) {
-    load_k(tm, lds_k0);
-    if (T > 1) load_k(tv, lds_k1);
-    load_v(tm, lds_v0);
+    load_k(tc, lds_k0);
+    if (T > 1) load_k(tn, lds_k1);
+    load_v(tc, lds_v0);
     wait_vmem_all();
     __syncthreads();
-    f32x16 sa, sb;
-    u64 pa[2], pb[2];
-    sa = qk_sub(lds_k0, 0);
-    sub(tm.kpos, sa, sb, pa, pb, lds_k0, 1, lds_v0, 0, Yes{}, Yes{}, No{});
-    int n = 0;
-    for (; n + 2 < T; n += 2) {
-      barrier_and_prefetch(n, lds_k0, lds_v1);
-      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k1, 0, lds_v0, 0, Yes{}, Yes{}, Yes{});
-      sub(tv.kpos, sa, sb, pa, pb, lds_k1, 1, lds_v0, 1, Yes{}, Yes{}, Yes{});
-      advance();
-      barrier_and_prefetch(n + 1, lds_k1, lds_v0);
-      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k0, 0, lds_v1, 0, Yes{}, Yes{}, Yes{});
-      sub(tv.kpos, sa, sb, pa, pb, lds_k0, 1, lds_v1, 1, Yes{}, Yes{}, Yes{});
-      advance();
-    }
-    if (n + 1 < T) {
-      barrier_and_prefetch(n, lds_k0, lds_v1);
-      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k1, 0, lds_v0, 0, Yes{}, Yes{}, Yes{});
-      sub(tv.kpos, sa, sb, pa, pb, lds_k1, 1, lds_v0, 1, Yes{}, Yes{}, Yes{});
-      advance();
-      barrier_and_prefetch(n + 1, lds_k1, lds_v0);
-      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k0, 0, lds_v1, 0, Yes{}, No{}, Yes{});
-      sub(0, sa, sb, pa, pb, lds_k0, 0, lds_v1, 1, No{}, No{}, Yes{});
+    SS sa, sb;
+    i32x8 pa, pb;
+    float dummy = 0.f;
+    qk(lds_k0, sa);
+    barrier_and_prefetch(0);
+    if (T == 1) {
+      sub(tc.kpos, sa, sb, pa, pb, kb_c, kb_n, lds_v0, Yes{}, No{}, No{});
+      wait_vmem_all();
+      __syncthreads();
+      body(sb, sa, pb, pa, kb_n, lds_v0, dummy, No{}, No{}, Yes{});
     } else {
-      barrier_and_prefetch(n, lds_k1, lds_v1);
-      sub(tm.kpos + 32, sb, sa, pb, pa, lds_k1, 0, lds_v0, 0, Yes{}, No{}, Yes{});
-      sub(0, sa, sb, pa, pb, lds_k1, 0, lds_v0, 1, No{}, No{}, Yes{});
+      sub(tc.kpos, sa, sb, pa, pb, kb_c, kb_n, lds_v0, Yes{}, Yes{}, No{});
+      advance();
+      int u = 1;
+      // u odd: S(u) in sb, S(u+1) into sa; u even: the other way round
+      for (; u + 2 < T; u += 2) {
+        barrier_and_prefetch(u);
+        sub(tc.kpos, sb, sa, pb, pa, kb_c, kb_n, lds_v0, Yes{}, Yes{}, Yes{});
+        advance();
+        barrier_and_prefetch(u + 1);
+        sub(tc.kpos, sa, sb, pa, pb, kb_c, kb_n, lds_v1, Yes{}, Yes{}, Yes{});
+        advance();
+      }
+      if (u + 1 < T) {
+        // u = T-2 (odd): one full sub-iteration, then the last tile (even)
+        barrier_and_prefetch(u);
+        sub(tc.kpos, sb, sa, pb, pa, kb_c, kb_n, lds_v0, Yes{}, Yes{}, Yes{});
+        advance();
+        barrier_and_prefetch(u + 1);
+        sub(tc.kpos, sa, sb, pa, pb, kb_c, kb_n, lds_v1, Yes{}, No{}, Yes{});
+        wait_vmem_all();
+        __syncthreads();
+        body(sb, sa, pb, pa, kb_n, lds_v0, dummy, No{}, No{}, Yes{});
+      } else {
+        // u = T-1 (odd): the last tile
+        barrier_and_prefetch(u);
+        sub(tc.kpos, sb, sa, pb, pa, kb_c, kb_n, lds_v0, Yes{}, No{}, Yes{});
+        wait_vmem_all();
+        __syncthreads();
+        body(sa, sb, pa, pb, kb_n, lds_v1, dummy, No{}, No{}, Yes{});
+      }
     }
   }
 
