@@ -125,3 +125,55 @@ def test_fp8_ring_driver_matches_oracle(name, H, ranks, rows):
             el = max(el, float(np.max(np.abs(lse[0, h, local].cpu().numpy() - rl))))
         print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
         assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_fp8_step_few_visible_tiles(T):
+    """One fp8 step whose 256-row blocks see exactly T key tiles of 64: the kernel's pipeline has its own
+    prologue and drain for one, two and three tiles, and an odd or even count of tiles after them.  The key
+    chunk starts 8 positions past a tile boundary relative to the first row block, so the causal limit
+    crosses tiles mid-way and the block's first rows see no key at all (LSE -inf, output 0)."""
+    H, D = 2, 128
+    q_start, q_len = 1000, 512
+    kv_start = q_start + 256 - 64 * T + 8
+    q_tab = cp.CpChunks.make([q_start], q_len)
+    kv_tab = cp.CpChunks.make([kv_start], 64 * T)
+    _check_fp8_step(q_tab, kv_tab, H, D, seed=500 + T)
+
+
+def test_fp8_step_chunk_switching():
+    """Three key chunks of one tile each: one in the past, one crossing the first row block's diagonal and
+    one wholly in the future, so the tile cursor moves across chunks and skips the invisible one."""
+    q_tab = cp.CpChunks.make([1000], 512)
+    kv_tab = cp.CpChunks.make([0, 1100, 5000], 64)
+    _check_fp8_step(q_tab, kv_tab, 2, 128, seed=520)
+
+
+def _check_fp8_step(q_tab, kv_tab, H, D, seed):
+    print("[case] fp8 step", q_tab, kv_tab, "H", H, flush=True)
+    qpos, kpos = positions(q_tab), positions(kv_tab)
+    S = int(max(qpos.max(), kpos.max())) + 1
+    Q, K, V = workloads.make_qkv_scaled((1, H, S, D), seed)
+    (qc, sq), (kc, sk), (vc, sv) = quantize(Q.float()), quantize(K.float()), quantize(V.float())
+    Qd, Kd, Vd = (dequantize(c, s) for c, s in ((qc, sq), (kc, sk), (vc, sv)))
+    q = _gather(qc, q_tab).to(DEV)
+    k = _gather(kc, kv_tab).to(DEV)
+    vt = _gather(vc, kv_tab).view(torch.uint8).transpose(2, 3).contiguous().view(torch.float8_e4m3fn).to(DEV)
+    Sq = len(qpos)
+    o = torch.empty((1, H, Sq, D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((1, H, Sq), dtype=torch.float32, device=DEV)
+    out = torch.empty((1, H, Sq, D), dtype=torch.bfloat16, device=DEV)
+    scale = 1.0 / np.sqrt(D)
+    cp.cp_attn_step_fwd_fp8(q, k, vt, o, lse, out, q_tab, kv_tab, scale, sq, sk, sv, cp.CP_STEP_WRITE)
+    torch.cuda.synchronize()
+    out_h, lse_h = out.float().cpu().numpy(), lse.cpu().numpy()
+    eo = el = 0.0
+    for h in range(H):
+        ro, rl = oracle.masked_attention(Qd[0, h][qpos], qpos, Kd[0, h][kpos], Vd[0, h][kpos], kpos, scale)
+        empty = np.isinf(rl)
+        assert np.array_equal(np.isneginf(lse_h[0, h]), empty), "rows without a visible key"
+        assert not np.any(out_h[0, h][empty]), "rows without a visible key must be 0"
+        eo = max(eo, float(np.max(np.abs(out_h[0, h][~empty] - ro[~empty]))))
+        el = max(el, float(np.max(np.abs(lse_h[0, h][~empty] - rl[~empty]))))
+    print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
+    assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)
