@@ -247,6 +247,7 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
     }
     if constexpr (!kExp) return false;
     lsum = exps(s_cur, p_cur, -m_run);
+    // keeps the packing of P(u) inside this sub-iteration's interleaved VALU stream
     asm volatile("" ::"v"(p_cur));
     constexpr int kMfma = (kQK ? 2 * NK : 0) + (kPV ? NDB : 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -341,9 +342,10 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
     __syncthreads();
     SS sa, sb;
     i32x8 pa, pb;
-    float dummy = 0.f;
+    float dummy = 0.f;  // the row-sum output of the PV-only drain calls
     qk(lds_k0, sa);
     barrier_and_prefetch(0);
+    // each branch ends with the drain: O += V(T-1) P(T-1), once V(T-1) has landed
     if (T == 1) {
       sub(tc.kpos, sa, sb, pa, pb, kb_c, kb_n, lds_v0, Yes{}, No{}, No{});
       wait_vmem_all();
