@@ -438,6 +438,9 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
     }
 }
 
+// Eight waves (256 rows), two per SIMD, held to 248 VGPRs like the bf16 step
+// kernel, so that registers stay free for the waves of a concurrent staging
+// copy on the copy stream.
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_num_vgpr(124))) fp8_step_kernel(const Fp8StepArgs a) {
   fp8_step_body(a);
 }
