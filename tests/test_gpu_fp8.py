@@ -177,3 +177,42 @@ def _check_fp8_step(q_tab, kv_tab, H, D, seed):
         el = max(el, float(np.max(np.abs(lse_h[0, h][~empty] - rl[~empty]))))
     print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
     assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)
+
+
+@pytest.mark.parametrize("rank", [0, 1])
+def test_fp8_ring_batch_heads_xcd_mapping(rank):
+    """Batch 2 x 4 heads: B*H = 8 is a multiple of the eight XCDs, so the launches use the XCD-aware
+    block-to-head mapping (every other fp8 case here has B*H = 2).  The ring driver against the oracle on
+    every row of every (batch, head)."""
+    B, H, D, N, L = 2, 4, 128, 2, 512
+    S = 2 * N * L
+    Q, K, V = workloads.make_qkv_scaled((B, H, S, D), 610 + rank)
+    (qc, sq), (kc, sk), (vc, sv) = quantize(Q.float()), quantize(K.float()), quantize(V.float())
+    Qd, Kd, Vd = (dequantize(c, s) for c, s in ((qc, sq), (kc, sk), (vc, sv)))
+    scale = 1.0 / np.sqrt(D)
+    print("[case] fp8 ring B", B, "H", H, "N", N, "L", L, "rank", rank, flush=True)
+    q_tab, kv_tabs = zigzag_tables(N, rank, L)
+    q = _gather(qc, q_tab).to(DEV)
+    ks = [_gather(kc, t).to(DEV) for t in kv_tabs]
+    vts = [_gather(vc, t).view(torch.uint8).transpose(2, 3).contiguous().view(torch.float8_e4m3fn).to(DEV)
+           for t in kv_tabs]
+    Sq = q.shape[2]
+    ws = torch.empty(cp.cp_ring_attn_fwd_fp8_workspace_bytes(B, H, ks[0].shape[2], D, Sq), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty((B, H, Sq, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+    cp.cp_ring_attn_fwd_fp8(q, q_tab, ks, vts, kv_tabs, out, lse, scale, sq, sk, sv, ws,
+                            copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    qpos = positions(q_tab)
+    out_h, lse_h = out.float().cpu().numpy(), lse.cpu().numpy()
+    eo = el = 0.0
+    for b in range(B):
+        for h in range(H):
+            kmax = int(qpos.max()) + 1
+            ro, rl = oracle.masked_attention(Qd[b, h][qpos], qpos, Kd[b, h, :kmax], Vd[b, h, :kmax],
+                                             np.arange(kmax), scale)
+            eo = max(eo, float(np.max(np.abs(out_h[b, h] - ro))))
+            el = max(el, float(np.max(np.abs(lse_h[b, h] - rl))))
+    print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
+    assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)
