@@ -129,8 +129,8 @@ def cpu_baseline_bwd(w, rank, budget_s, Q, K, V, kv_tabs):
     }
 
 
-def bwd_traffic(workload, kernel):
-    """Calibrated HBM bytes per launch of a backward kernel, from its counter
+def kernel_traffic(workload, kernel):
+    """Calibrated HBM bytes per launch of a kernel, from its counter
     summary, only if taken on this workload and on the kernel source built now."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     try:
@@ -276,7 +276,7 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
             "kernel": f"bwd_{dom}_kernel<128>", "bound": "mfma",
             "achieved": kernels[dom]["achieved"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(kernels[dom]["achieved"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": bwd_traffic(w.name, f"bwd_{dom}_kernel"),
+            "traffic": kernel_traffic(w.name, f"bwd_{dom}_kernel"),
             "kernels": kernels, "kernel_ms_per_step": round(N * (dq_ms + dkdv_ms), 5),
         },
         "timing": {
@@ -554,6 +554,85 @@ def copy_probe(mib, reps):
           flush=True)
 
 
+def bench_merge(args, w, stream):
+    """The standalone log-sum-exp merge (cp_attn_merge) at the rank share's
+    shape: fp32 (O, LSE) pairs [B,H,2L,D] / [B,H,2L] merged in place, with the
+    bf16 finalize.  Inputs are seeded: O ~ N(0, 1), LSE ~ N(0, 4) with one row
+    in 16 of each operand -inf (an empty partial).  HBM-bound: per row the
+    call reads two (O, LSE) pairs and writes one, plus the bf16 row, so the
+    algorithmic bytes are B*H*2L*(3*4*D + 3*4 + 2*D).  Repeated calls merge the
+    same partial into the evolving accumulator, which stays finite: each O row
+    is a convex combination of finite rows, and after n calls
+    exp(LSE) = exp(LSE_0) + n exp(LSE_part)."""
+    import torch
+    import long_sequence_causal_cp_amd as cp
+
+    dev = torch.device("cuda:0")
+    B, H, D, Sq = w.B, w.H, w.D, 2 * w.chunk_len
+    g = torch.Generator().manual_seed(7000 + w.seed)
+
+    def pair():
+        o = torch.randn((B, H, Sq, D), generator=g)
+        l = 2.0 * torch.randn((B, H, Sq), generator=g)
+        l[torch.rand((B, H, Sq), generator=g) < 1.0 / 16] = float("-inf")
+        return o.to(dev), l.to(dev)
+
+    o_acc, lse_acc = pair()
+    o_part, lse_part = pair()
+    out = torch.empty((B, H, Sq, D), dtype=torch.bfloat16, device=dev)
+    nbytes = B * H * Sq * (3 * 4 * D + 3 * 4 + 2 * D)
+
+    # one call checked by properties: the merged LSE is at least either input's, everything finite
+    l_before = torch.maximum(lse_acc, lse_part)
+    cp.cp_attn_merge(o_acc, lse_acc, o_part, lse_part, out, stream=stream)
+    torch.cuda.synchronize()
+    ok = bool(torch.all((lse_acc >= l_before) | torch.isneginf(l_before))) and bool(torch.isfinite(o_acc).all()) \
+        and bool(torch.isfinite(out.float()).all())
+    both_empty = torch.isneginf(l_before)
+    ok = ok and bool(torch.isneginf(lse_acc[both_empty]).all())
+    assert ok, "merge property check failed"
+
+    def step():
+        cp.cp_attn_merge(o_acc, lse_acc, o_part, lse_part, out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(f"[bench merge] {w.describe()} rank share {B}x{H}x{Sq}x{D}: {ms * 1e3:.2f} us per merge, "
+          f"{gbs:.0f} GB/s of {nbytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+    res = {
+        "metric": "HBM GB/s of the standalone LSE merge (cp_attn_merge, in place, with bf16 finalize) on one "
+                  "CP-rank share; % of 8 TB/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: rank share of cp={w.cp}, (O, LSE) fp32 [B={B}, H={H}, {Sq}, D={D}] pairs, "
+                        "one row in 16 of each operand empty",
+            "seq_len": w.S, "cp": w.cp, "B": B, "H": H, "D": D, "rows": B * H * Sq,
+            "bytes_per_merge": nbytes, "wall_s_timed": round(wall, 4),
+        },
+        "roofline": {
+            "kernel": "merge_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": kernel_traffic(w.name, "merge_kernel"),
+            "launches_per_step": 1,
+            "avg_launch_ms": round(ms, 5),
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -564,10 +643,11 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "step_kernel_s32k_cp8_traffic.json"))
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "allgather", "fp8"), default="fwd",
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "allgather", "fp8", "merge"), default="fwd",
                     help="fwd: the ring forward (headline); bwd: the rank's backward ring steps; allgather: "
                          "the rank's queries against the gathered keys of the whole sequence in one step; fp8: "
-                         "the share's ring steps in fp8 (cp_attn_step_fwd_fp8 per step)")
+                         "the share's ring steps in fp8 (cp_attn_step_fwd_fp8 per step); merge: the standalone "
+                         "LSE merge (cp_attn_merge) at the share's shape")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB --steps times (counter calibration)")
     args = ap.parse_args()
@@ -590,6 +670,8 @@ def main():
     dev = torch.device("cuda:0")
     w = workloads.get(args.workload)
     L, N, r = w.chunk_len, w.cp, args.rank
+    if args.pass_ == "merge":
+        return bench_merge(args, w, torch.cuda.current_stream())
     Q, K, V = workloads.make_qkv(w)
 
     def gather(x, t):
