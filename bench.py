@@ -144,6 +144,46 @@ def kernel_traffic(workload, kernel):
     return None
 
 
+# ---- the rest of the cpu_baseline leg: the oracle's reference values for the
+# few rows each pass spot-checks after its timed region (head (0, 0)) ----
+def cpu_baseline_rows(w, rank, Q, K, V, rows):
+    """The oracle's (out, LSE) of the rank's local query rows ``rows``."""
+    import oracle
+    pos = oracle.local_positions(w.S, w.cp, rank)
+    return oracle.causal_attention_rows(oracle.to_f64(Q[0, 0]), oracle.to_f64(K[0, 0]), oracle.to_f64(V[0, 0]),
+                                        pos[rows], w.scale)
+
+
+def cpu_baseline_rows_fp8(w, rank, qd, kd, vd, rows):
+    """The oracle's (out, LSE) of local rows ``rows`` on dequantised fp8 values
+    (qd, kd, vd: float64 [S, D] in natural token order)."""
+    import numpy as np
+    import oracle
+    pos = oracle.local_positions(w.S, w.cp, rank)
+    kmax = int(pos[rows].max()) + 1
+    return oracle.masked_attention(qd[pos[rows]], pos[rows], kd[:kmax], vd[:kmax], np.arange(kmax), w.scale)
+
+
+def cpu_baseline_grads(w, rank, Q, K, V, dO, rows, keys):
+    """The oracle's dQ of local rows ``rows`` (over every visible key) and the
+    dK, dV contributions of this rank's queries to keys ``keys`` of its own
+    block."""
+    import numpy as np
+    import oracle
+    pos = oracle.local_positions(w.S, w.cp, rank)
+    f64 = lambda X: oracle.to_f64(X[0, 0])
+    Qh, Kh, Vh, dOh = f64(Q), f64(K), f64(V), f64(dO)
+    kmax = int(pos[rows].max()) + 1
+    o_r, l_r = oracle.causal_attention_rows(Qh, Kh, Vh, pos[rows], w.scale)
+    dq_ref, _, _ = oracle.masked_attention_grad(Qh[pos[rows]], pos[rows], Kh[:kmax], Vh[:kmax], np.arange(kmax),
+                                                dOh[pos[rows]], o_r, l_r, w.scale)
+    o_all, l_all = oracle.causal_attention_rows(Qh, Kh, Vh, pos, w.scale)
+    kpos = pos[keys]
+    _, dk_ref, dv_ref = oracle.masked_attention_grad(Qh[pos], pos, Kh[kpos], Vh[kpos], kpos, dOh[pos], o_all, l_all,
+                                                     w.scale)
+    return dq_ref, dk_ref, dv_ref
+
+
 def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream, gather):
     """The rank's backward share: one cp_ring_attn_bwd call.
 
@@ -158,7 +198,6 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
     """
     import numpy as np
     import torch
-    import oracle
     import workloads
     import long_sequence_causal_cp_amd as cp
 
@@ -230,21 +269,10 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
     # writes them, so they hold this rank's contribution alone)
     step()
     torch.cuda.synchronize()
-    pos = oracle.local_positions(w.S, N, r)
     L = w.chunk_len
-    f64 = lambda X: oracle.to_f64(X[0, 0])
-    Qh, Kh, Vh = f64(Q), f64(K), f64(V)
-    dOh = oracle.to_f64(workloads.make_grad_out(w)[0, 0])
     rows = np.array([0, L - 1, L, 2 * L - 1])
-    kmax = int(pos[rows].max()) + 1
-    o_r, l_r = oracle.causal_attention_rows(Qh, Kh, Vh, pos[rows], w.scale)
-    dq_ref, _, _ = oracle.masked_attention_grad(Qh[pos[rows]], pos[rows], Kh[:kmax], Vh[:kmax], np.arange(kmax),
-                                                dOh[pos[rows]], o_r, l_r, w.scale)
-    o_all, l_all = oracle.causal_attention_rows(Qh, Kh, Vh, pos, w.scale)
     keys = np.array([0, L - 1, L, 2 * L - 1])
-    kpos0 = oracle.local_positions(w.S, N, r)
-    _, dk_ref, dv_ref = oracle.masked_attention_grad(Qh[pos], pos, Kh[kpos0[keys]], Vh[kpos0[keys]], kpos0[keys],
-                                                     dOh[pos], o_all, l_all, w.scale)
+    dq_ref, dk_ref, dv_ref = cpu_baseline_grads(w, r, Q, K, V, workloads.make_grad_out(w), rows, keys)
     rel = lambda got, ref: float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
     check = {"dq_rel": rel(dq[0, 0, rows].cpu().numpy(), dq_ref),
              "dk_rel": rel(dks[0][0, 0, keys].cpu().numpy(), dk_ref),
@@ -300,7 +328,6 @@ def bench_allgather(args, w, Q, K, V, q, q_tab, kv_tabs, stream):
     """
     import numpy as np
     import torch
-    import oracle
     import long_sequence_causal_cp_amd as cp
 
     B, H, Sq, D = q.shape
@@ -338,11 +365,9 @@ def bench_allgather(args, w, Q, K, V, q, q_tab, kv_tabs, stream):
     cp.cp_profile_enable(False)
     avg = statistics.fmean(kern_ms)
     achieved = flops / (avg * 1e-3) / 1e12
-    pos = oracle.local_positions(w.S, w.cp, args.rank)
     L = w.chunk_len
     rows = np.array([0, L - 1, L, 2 * L - 1])
-    ro, rl = oracle.causal_attention_rows(oracle.to_f64(Q[0, 0]), oracle.to_f64(K[0, 0]), oracle.to_f64(V[0, 0]),
-                                          pos[rows], w.scale)
+    ro, rl = cpu_baseline_rows(w, args.rank, Q, K, V, rows)
     eo = float(np.max(np.abs(out[0, 0, rows].float().cpu().numpy() - ro)))
     el = float(np.max(np.abs(lse[0, 0, rows].cpu().numpy() - rl)))
     gather_bytes = 2 * B * H * (w.S - Sq) * D * 2
@@ -386,7 +411,6 @@ def bench_fp8(args, w, Q, K, V, q_tab, kv_tabs, stream):
     import math as _m
     import numpy as np
     import torch
-    import oracle
     import long_sequence_causal_cp_amd as cp
 
     dev = torch.device("cuda:0")
@@ -497,13 +521,10 @@ def bench_fp8(args, w, Q, K, V, q_tab, kv_tabs, stream):
     ring8()
     torch.cuda.synchronize()
 
-    pos = oracle.local_positions(w.S, w.cp, args.rank)
     L = w.chunk_len
     rows = np.array([0, L - 1, L, 2 * L - 1])
     deq = lambda c, sc: c.to(torch.float64).numpy() * sc
-    kmax = int(pos[rows].max()) + 1
-    ro, rl = oracle.masked_attention(deq(qc[0, 0], sq)[pos[rows]], pos[rows], deq(kc[0, 0, :kmax], sk),
-                                     deq(vc[0, 0, :kmax], sv), np.arange(kmax), w.scale)
+    ro, rl = cpu_baseline_rows_fp8(w, args.rank, deq(qc[0, 0], sq), deq(kc[0, 0], sk), deq(vc[0, 0], sv), rows)
     eo = float(np.max(np.abs(out[0, 0, rows].float().cpu().numpy() - ro)))
     el = float(np.max(np.abs(lse[0, 0, rows].cpu().numpy() - rl)))
     print(f"[bench fp8] {w.describe()} rank {args.rank}: ring {ms_per_step:.4f} ms/step, {value:.1f} TFLOP/s "
@@ -788,12 +809,9 @@ def main():
         except (OSError, ValueError, KeyError):
             traffic = None
 
-    # spot check a few rows against the oracle (outside the timed region)
-    import oracle
-    pos = oracle.local_positions(w.S, N, r)
+    # spot check a few rows against the oracle's (outside the timed region)
     rows = np.array([0, L - 1, L, 2 * L - 1])
-    ro, rl = oracle.causal_attention_rows(oracle.to_f64(Q[0, 0]), oracle.to_f64(K[0, 0]),
-                                          oracle.to_f64(V[0, 0]), pos[rows], w.scale)
+    ro, rl = cpu_baseline_rows(w, r, Q, K, V, rows)
     eo = float(np.max(np.abs(out[0, 0, rows].float().cpu().numpy() - ro)))
     el = float(np.max(np.abs(lse[0, 0, rows].cpu().numpy() - rl)))
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.1f} TFLOP/s; "
