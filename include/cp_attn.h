@@ -129,7 +129,7 @@ cp_status_t cp_attn_step_fwd(const void* q, const void* k, const void* v,
  * The scores use softmax_scale * q_scale * k_scale; the probabilities are
  * rounded to e4m3 for the PV product (fp32 accumulation) and the output is
  * multiplied by v_scale.
- * Supported: D = 128, q chunk_len a multiple of 256; other shapes return
+ * Supported: D = 128, q chunk_len a multiple of 128; other shapes return
  * CP_ERR_UNSUPPORTED.  Scales must be finite and > 0.  Errors otherwise as
  * cp_attn_step_fwd.
  */
@@ -270,7 +270,7 @@ size_t cp_ring_attn_fwd_fp8_workspace_bytes(int B, int H, int Skv, int D, int Sq
  *   out        bf16 [B,H,Sq,D]; lse fp32 [B,H,Sq]
  *   scales     as cp_attn_step_fwd_fp8
  * The staging copies move one byte per value, half of the bf16 ring's.
- * Supported: D = 128, q chunk_len a multiple of 256.  Errors as
+ * Supported: D = 128, q chunk_len a multiple of 128.  Errors as
  * cp_ring_attn_fwd; CP_ERR_UNSUPPORTED for other shapes.
  */
 cp_status_t cp_ring_attn_fwd_fp8(const void* q, const cp_chunks_t* q_chunks,

@@ -454,9 +454,9 @@ cp_status_t cp_attn_step_fwd_fp8(const void* q, const void* k, const void* vt, f
   if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
   if ((st = check_chunks(kv_chunks, "kv_chunks")) != CP_OK) return st;
   if (D != 128) return fail(CP_ERR_UNSUPPORTED, "fp8 step: head dim D = %d not built (128)", D);
-  if (q_chunks->chunk_len % cpattn::kFp8BlockRows != 0)
+  if (q_chunks->chunk_len % cpattn::kFp8RowQuantum != 0)
     return fail(CP_ERR_UNSUPPORTED, "fp8 step: q chunk_len = %d must be a multiple of %d", q_chunks->chunk_len,
-                cpattn::kFp8BlockRows);
+                cpattn::kFp8RowQuantum);
   const float sc[3] = {q_scale, k_scale, v_scale};
   for (float x : sc)
     if (!std::isfinite(x) || !(x > 0.f)) return fail(CP_ERR_INVALID, "fp8 step: scales must be finite and > 0");
@@ -496,7 +496,6 @@ cp_status_t cp_attn_step_fwd_fp8(const void* q, const void* k, const void* vt, f
     a.vtc[i] = static_cast<const uint8_t*>(vt) + (size_t)i * kv_chunks->chunk_len;
     a.kv_start[i] = (int)kv_chunks->start[i];
   }
-  a.rb_per_chunk = q_chunks->chunk_len / cpattn::kFp8BlockRows;
   a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
   a.scale_log2 = softmax_scale * q_scale * k_scale * 1.4426950408889634f;
   a.v_scale = v_scale;
@@ -692,9 +691,9 @@ cp_status_t cp_ring_attn_fwd_fp8(const void* q, const cp_chunks_t* q_chunks, con
   if (n_steps < 1 || n_steps > CP_MAX_STEPS)
     return fail(CP_ERR_INVALID, "n_steps = %d outside [1, %d]", n_steps, CP_MAX_STEPS);
   if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
-  if (q_chunks->chunk_len % cpattn::kFp8BlockRows != 0)
+  if (q_chunks->chunk_len % cpattn::kFp8RowQuantum != 0)
     return fail(CP_ERR_UNSUPPORTED, "fp8 ring: q chunk_len = %d must be a multiple of %d", q_chunks->chunk_len,
-                cpattn::kFp8BlockRows);
+                cpattn::kFp8RowQuantum);
   const float sc[3] = {q_scale, k_scale, v_scale};
   for (float x : sc)
     if (!std::isfinite(x) || !(x > 0.f)) return fail(CP_ERR_INVALID, "fp8 ring: scales must be finite and > 0");
@@ -758,8 +757,7 @@ cp_status_t cp_ring_attn_fwd_fp8(const void* q, const cp_chunks_t* q_chunks, con
                          a.kv_start[a.n_kv_chunks] = (int)t.start[c];
                        }
                      }
-                     a.rb_per_chunk = q_chunks->chunk_len / cpattn::kFp8BlockRows;
-                     a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+                                        a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
                      a.scale_log2 = softmax_scale * q_scale * k_scale * 1.4426950408889634f;
                      a.v_scale = v_scale;
                      std::vector<int> idx(rl.active);

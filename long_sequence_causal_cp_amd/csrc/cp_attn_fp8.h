@@ -28,14 +28,18 @@ struct Fp8StepArgs {
   int flags[kMaxChunks];           // kFlagMerge, kFlagWriteO, kFlagFinalize
   int q_start[kMaxChunks];
   int kv_start[kMaxChunks];
-  int rb_per_chunk;
+  int rb_per_chunk;                // set by launch_step_fp8 from its row-block choice
   int heads_per_xcd;
   float scale_log2;                // tau * q_scale * k_scale * log2(e)
   float v_scale;                   // the dequantisation factor of V
 };
 
-// Rows per workgroup of the fp8 step kernel (D = 128, chunks of a multiple of it).
+// Rows per workgroup of the fp8 step kernel (D = 128): 256, or 128 where a grid
+// of 256-row workgroups would leave compute units idle or the query chunk
+// length is not a multiple of 256.  Query chunk lengths must be multiples of
+// kFp8RowQuantum.
 constexpr int kFp8BlockRows = 256;
+constexpr int kFp8RowQuantum = 128;
 
 hipError_t launch_step_fp8(const Fp8StepArgs& a, hipStream_t stream);
 

@@ -48,7 +48,6 @@ namespace {
 
 
 constexpr int kD8 = 128;          // head dimension of the fp8 kernel
-constexpr int kNW8 = 8;           // waves per workgroup, 32 rows each
 constexpr int kTB8 = kTileKeys * kD8;  // bytes of one K or V^T tile
 constexpr float kSumLimit8 = 256.0f;
 
@@ -63,10 +62,11 @@ __device__ __forceinline__ float half_sum8(float x) {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+template <int NW>
 __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
   constexpr int D = kD8;
-  constexpr int NW = kNW8;
   constexpr int BM = 32 * NW;
+  constexpr int LPW = 8 / NW;  // direct-to-LDS instructions per wave per K or V^T tile (8 KiB)
   constexpr int NK = D / 64;   // k-steps of the QK^T product
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
   constexpr int TB = kTB8;
@@ -140,17 +140,25 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
     if (t.left <= 0) t = chunk_after(t.c);
     return t;
   };
-  // this wave's direct-to-LDS instruction of each tile writes LDS bytes
-  // [1024 wave, +1024): lane i the 16 bytes at 1024 wave + 16 i
-  unsigned k_ld, v_ld;
-  {
-    const int r = 8 * wave_u + lane / 8, pc = lane % 8;
-    k_ld = (unsigned)(r * D + 16 * (pc ^ ((r >> 1) & 7)));
-    const int dr = 16 * wave_u + lane / 4, pv = lane % 4;
-    v_ld = (unsigned)(dr * a.Skv + 16 * (pv ^ ((dr >> 2) & 3)));
+  // direct-to-LDS instruction i of this wave fills 1-KiB block b = wave + NW i
+  // of each tile: lane l the 16 bytes at 1024 b + 16 l
+  unsigned k_ld[LPW], v_ld[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int b = wave_u + NW * i;
+    const int r = 8 * b + lane / 8, pc = lane % 8;
+    k_ld[i] = (unsigned)(r * D + 16 * (pc ^ ((r >> 1) & 7)));
+    const int dr = 16 * b + lane / 4, pv = lane % 4;
+    v_ld[i] = (unsigned)(dr * a.Skv + 16 * (pv ^ ((dr >> 2) & 3)));
   }
-  auto load_k = [&](const Cursor& t, unsigned char* buf) { global_to_lds_16(t.kp, k_ld, buf + 1024 * wave_u); };
-  auto load_v = [&](const Cursor& t, unsigned char* buf) { global_to_lds_16(t.vp, v_ld, buf + 1024 * wave_u); };
+  auto load_k = [&](const Cursor& t, unsigned char* buf) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) global_to_lds_16(t.kp, k_ld[i], buf + 1024 * (wave_u + NW * i));
+  };
+  auto load_v = [&](const Cursor& t, unsigned char* buf) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) global_to_lds_16(t.vp, v_ld[i], buf + 1024 * (wave_u + NW * i));
+  };
 
   // Q^T fragments: lane holds Q[row lq][64 ks + 32 g .. + 32]
   i32x8 qreg[NK];
@@ -442,15 +450,43 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
 // kernel, so that registers stay free for the waves of a concurrent staging
 // copy on the copy stream.
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_num_vgpr(124))) fp8_step_kernel(const Fp8StepArgs a) {
-  fp8_step_body(a);
+  fp8_step_body<8>(a);
+}
+// Four waves (128 rows), two workgroups per CU under the same register budget:
+// for grids of 256-row workgroups that would leave compute units idle, and for
+// query chunk lengths that are multiples of 128 but not of 256.
+__global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_num_vgpr(124)))
+fp8_step_kernel_128(const Fp8StepArgs a) {
+  fp8_step_body<4>(a);
+}
+
+int fp8_device_cus() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      return cus;
+    return 256;
+  }();
+  return n;
 }
 
 }  // namespace
 
-hipError_t launch_step_fp8(const Fp8StepArgs& a, hipStream_t stream) {
+hipError_t launch_step_fp8(const Fp8StepArgs& args, hipStream_t stream) {
+  // A row's result does not depend on the row-block size (a block only decides
+  // which tiles it stages; keys past a row are masked), so the launch picks it:
+  // 256-row blocks unless their grid would leave compute units idle.
+  Fp8StepArgs a = args;
+  int bm = (a.q_chunk_len % 256 == 0) ? 256 : 128;
+  if (bm == 256 && (long long)a.n_order * (a.q_chunk_len / 256) * a.BH < fp8_device_cus()) bm = 128;
+  a.rb_per_chunk = a.q_chunk_len / bm;
   const long long grid = (long long)a.n_order * a.rb_per_chunk * a.BH;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fp8_step_kernel, dim3((unsigned)grid), dim3(64 * kNW8), 0, stream, a);
+  if (bm == 256)
+    hipLaunchKernelGGL(fp8_step_kernel, dim3((unsigned)grid), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fp8_step_kernel_128, dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

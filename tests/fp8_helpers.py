@@ -38,15 +38,33 @@ def round_e4m3(p: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.asarray(p, np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
-def emulated_error(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray, scale: float) -> float:
+def emulated_error(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray, scale: float,
+                   k_pos: np.ndarray | None = None) -> float:
     """Max |O_kernel_model - O_exact| over the rows q [n, D] at positions q_pos
-    (keys k, v [m, D] at positions 0..m-1, causal)."""
+    that see at least one key (keys k, v [m, D] at positions k_pos, by default
+    0..m-1; causal)."""
+    k_pos = np.arange(k.shape[0]) if k_pos is None else np.asarray(k_pos)
     s = scale * (q @ k.T)
-    vis = np.arange(k.shape[0])[None, :] <= q_pos[:, None]
-    s = np.where(vis, s, -np.inf)
+    vis = k_pos[None, :] <= np.asarray(q_pos)[:, None]
+    has = vis.any(axis=1)
+    s, vis = np.where(vis, s, -np.inf)[has], vis[has]
+    if s.shape[0] == 0:
+        return 0.0
     m = s.max(axis=1, keepdims=True)
     p = np.where(vis, np.exp(s - m), 0.0)
     l = p.sum(axis=1, keepdims=True)
     exact = (p @ v) / l
     model = (round_e4m3(p) @ v) / l
     return float(np.max(np.abs(model - exact)))
+
+
+# The fp8 output tolerance is this multiple of the model's deviation: on the
+# zigzag workloads the model gives 0.035-0.039 and the bound there is 0.1.
+# Rows that see few keys (near a chunk start, or crafted key tables) average
+# the rounding over fewer terms, so their bound comes from the model on the
+# same inputs with the same margin.
+MODEL_MARGIN = 2.5
+
+
+def out_tolerance(model_error: float, floor: float) -> float:
+    return max(floor, MODEL_MARGIN * model_error)

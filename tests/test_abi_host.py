@@ -255,7 +255,7 @@ def test_empty_merge_and_delta_need_no_pointers(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(D=64), cb.CP_ERR_UNSUPPORTED),
-    (dict(qt=cb.CpChunks.make([0, 192], 64)), cb.CP_ERR_UNSUPPORTED),      # q chunks not a multiple of 256
+    (dict(qt=cb.CpChunks.make([0, 192], 64)), cb.CP_ERR_UNSUPPORTED),      # q chunks not a multiple of 128
     (dict(vs=0.0), cb.CP_ERR_INVALID),
     (dict(qs=float("nan")), cb.CP_ERR_INVALID),
     (dict(mode=3), cb.CP_ERR_INVALID),
