@@ -476,8 +476,28 @@ int bwd_dq_rows(int q_chunk_len) {
 }
 int bwd_dkdv_keys(int kv_chunk_len) { return (kv_chunk_len % 256 == 0) ? 256 : (kv_chunk_len % 128 == 0) ? 128 : 64; }
 
+namespace {
+int bwd_device_cus() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      return cus;
+    return 256;
+  }();
+  return n;
+}
+}  // namespace
+
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
-  const int bm = bwd_dq_rows(a.q_chunk_len);
+  // The grid covers every query row of the rank, and in a ring step past the
+  // first the rows of one chunk see no key (their workgroups end at once).  Where
+  // a grid of 256-row workgroups holds at most one per compute unit, 128-row
+  // ones spread the busy rows over twice as many units.  A row's dQ does not
+  // depend on the choice: its wave sums the same key tiles in the same order,
+  // and the tiles a larger block adds are masked to exact zeros.
+  int bm = bwd_dq_rows(a.q_chunk_len);
+  if (bm == 256 && (long long)a.BH * (a.Sq / 256) <= bwd_device_cus()) bm = 128;
   const long long grid = (long long)a.BH * (a.Sq / bm);
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk((unsigned)(2 * bm));  // one wave per 32 rows
