@@ -559,8 +559,15 @@ hipError_t launch_step(const StepArgs& args, int D, hipStream_t stream) {
   // Every row's result is the same whatever the row-block size (a row block
   // only decides which tiles are staged; tiles past a row are masked to exact
   // zeros), so the launch picks it: 256-row blocks unless their grid would
-  // leave compute units idle.
-  if (bm == 256 && (long long)a.n_order * (a.q_chunk_len / 256) * a.BH < device_cus()) bm = 128;
+  // leave compute units idle, or would give each unit exactly one block of a
+  // launch that holds a diagonal chunk pair (its blocks' work then ranges from
+  // a few tiles to twice the mean, and 128-row blocks, two per unit, let the
+  // light ones finish beside the heavy ones).
+  bool diag = false;
+  for (int i = 0; i < a.n_order; ++i)
+    for (int k = 0; k < a.n_kv_chunks; ++k) diag = diag || a.q_start[a.order[i]] == a.kv_start[k];
+  const long long g256 = (long long)a.n_order * (a.q_chunk_len / 256) * a.BH;
+  if (bm == 256 && (g256 < device_cus() || (diag && g256 <= device_cus()))) bm = 128;
   a.rb_per_chunk = a.q_chunk_len / bm;
   const long long grid = (long long)a.n_order * a.rb_per_chunk * a.BH;
   if (grid <= 0) return hipSuccess;
