@@ -476,10 +476,17 @@ int fp8_device_cus() {
 hipError_t launch_step_fp8(const Fp8StepArgs& args, hipStream_t stream) {
   // A row's result does not depend on the row-block size (a block only decides
   // which tiles it stages; keys past a row are masked), so the launch picks it:
-  // 256-row blocks unless their grid would leave compute units idle.
+  // 256-row blocks unless their grid would leave compute units idle, or would
+  // give each unit exactly one block of a launch that holds a diagonal chunk
+  // pair (block work then ranges from a few tiles to twice the mean; two
+  // 128-row blocks per unit let the light ones finish beside the heavy ones).
   Fp8StepArgs a = args;
   int bm = (a.q_chunk_len % 256 == 0) ? 256 : 128;
-  if (bm == 256 && (long long)a.n_order * (a.q_chunk_len / 256) * a.BH < fp8_device_cus()) bm = 128;
+  bool diag = false;
+  for (int i = 0; i < a.n_order; ++i)
+    for (int k = 0; k < a.n_kv_chunks; ++k) diag = diag || a.q_start[a.order[i]] == a.kv_start[k];
+  const long long g256 = (long long)a.n_order * (a.q_chunk_len / 256) * a.BH;
+  if (bm == 256 && (g256 < fp8_device_cus() || (diag && g256 <= fp8_device_cus()))) bm = 128;
   a.rb_per_chunk = a.q_chunk_len / bm;
   const long long grid = (long long)a.n_order * a.rb_per_chunk * a.BH;
   if (grid <= 0) return hipSuccess;
