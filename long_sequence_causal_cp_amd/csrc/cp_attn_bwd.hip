@@ -514,7 +514,16 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  const int bn = bwd_dkdv_keys(a.kv_chunk_len);
+  // As for the forward: a grid of 256-key workgroups with exactly one per
+  // compute unit, in a step that holds a diagonal chunk pair, has blocks whose
+  // work ranges from a few query tiles to twice the mean; 128-key blocks, two
+  // per unit, let the light ones finish beside the heavy ones.  A key's dK, dV
+  // are the same either way (its wave sums the same query tiles in order).
+  int bn = bwd_dkdv_keys(a.kv_chunk_len);
+  bool diag = false;
+  for (int i = 0; i < a.n_q_chunks; ++i)
+    for (int k = 0; k < a.n_kv_chunks; ++k) diag = diag || a.q_start[i] == a.kv_start[k];
+  if (bn == 256 && diag && (long long)a.BH * (a.Skv / 256) <= bwd_device_cus()) bn = 128;
   const long long grid = (long long)a.BH * (a.Skv / bn);
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk((unsigned)(2 * bn));  // one wave per 32 keys
