@@ -49,11 +49,37 @@ def visible_pairs(q_tab, kv_tabs):
     return total
 
 
-def cpu_baseline(w, rank, budget_s, Q, K, V):
+def settle(fn, stream, batch=5, tol=0.01, window=3, max_calls=400):
+    """Untimed clock settling: run ``fn`` in batches of ``batch`` calls until the
+    mean call time of the last ``window`` batches agrees within ``tol``
+    (max/min - 1), at most ``max_calls`` calls.  After host-side setup the GPU
+    runs the first few dozen forwards slower while its clocks ramp up; the
+    timed region starts only once they have settled.  Returns the number of
+    calls and the last batch's mean milliseconds."""
+    import torch
+    times, n = [], 0
+    while n < max_calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / batch)
+        n += batch
+        last = times[-window:]
+        if len(last) == window and max(last) <= (1.0 + tol) * min(last):
+            break
+    return n, times[-1]
+
+
+def cpu_baseline(w, rank, budget_s, Q, K, V, keep=None):
     """Time the fp64 oracle on a bounded sample of the same share.
 
     The sample is the rank's full set of query rows for as many (batch, head)
     pairs as fit in ``budget_s`` seconds (at least one head), taken in order.
+    If ``keep`` is a dict, the oracle's (out, lse) of each computed head is
+    stored in it under (b, h), for the bench's parity check.
     """
     import numpy as np
     import oracle
@@ -71,7 +97,9 @@ def cpu_baseline(w, rank, budget_s, Q, K, V):
     done, pairs, t0 = 0, 0, time.perf_counter()
     for b, h in heads:
         q, k, v = (oracle.to_f64(x[b, h]) for x in (Q, K, V))
-        oracle.causal_attention_rows(q, k, v, pos, w.scale)
+        res = oracle.causal_attention_rows(q, k, v, pos, w.scale)
+        if keep is not None:
+            keep[(b, h)] = res
         pairs += int((pos + 1).sum())
         done += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -221,7 +249,9 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench bwd] {w.describe()} rank {r}: warmup {args.warmup} done", file=sys.stderr, flush=True)
+    settle_n = settle(step, stream)[0] if args.settle else 0
+    print(f"[bench bwd] {w.describe()} rank {r}: warmup {args.warmup} done, settled after {settle_n} more",
+          file=sys.stderr, flush=True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -237,9 +267,12 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    kern_ms = cp.cp_profile_read(8192)
+    kern = cp.cp_profile_read_named(8192)
     cp.cp_profile_enable(False)
+    kern_ms = [t for t, _ in kern]
     assert len(kern_ms) == 2 * N * args.steps, (len(kern_ms), N, args.steps)
+    dq_names = sorted(set(n for _, n in kern[0::2]))
+    dkdv_names = sorted(set(n for _, n in kern[1::2]))
     dq_ms = statistics.fmean(kern_ms[0::2])
     dkdv_ms = statistics.fmean(kern_ms[1::2])
     dq_flop = 6.0 * D * B * H * pairs / N      # per launch, averaged over the ring steps
@@ -287,6 +320,7 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_forwards": settle_n,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -301,7 +335,7 @@ def bench_backward(args, w, Q, K, V, q, q_tab, ks, vs, kv_tabs, out, lse, stream
             "visible_pairs_per_head": pairs, "flop_per_step": flops, "wall_s_timed": round(wall, 4),
         },
         "roofline": {
-            "kernel": f"bwd_{dom}_kernel<128>", "bound": "mfma",
+            "kernel": " + ".join(dkdv_names if dom == "dkdv" else dq_names), "bound": "mfma",
             "achieved": kernels[dom]["achieved"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(kernels[dom]["achieved"] / PEAK_BF16_TFLOPS, 4),
             "traffic": kernel_traffic(w.name, f"bwd_{dom}_kernel"),
@@ -347,6 +381,8 @@ def bench_allgather(args, w, Q, K, V, q, q_tab, kv_tabs, stream):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.settle:
+        settle(step, stream)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -361,8 +397,10 @@ def bench_allgather(args, w, Q, K, V, q, q_tab, kv_tabs, stream):
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    kern_ms = cp.cp_profile_read(8192)
+    kern = cp.cp_profile_read_named(8192)
     cp.cp_profile_enable(False)
+    kern_ms = [t for t, _ in kern]
+    ag_names = sorted(set(n for _, n in kern))
     avg = statistics.fmean(kern_ms)
     achieved = flops / (avg * 1e-3) / 1e12
     L = w.chunk_len
@@ -387,7 +425,7 @@ def bench_allgather(args, w, Q, K, V, q, q_tab, kv_tabs, stream):
             "gather_bytes_not_timed": gather_bytes,
         },
         "roofline": {
-            "kernel": "step_kernel_256<128> over one K/V chunk of the whole sequence", "bound": "mfma",
+            "kernel": " + ".join(ag_names) + " over one K/V chunk of the whole sequence", "bound": "mfma",
             "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "launches_per_step": 1,
             "avg_launch_ms": round(avg, 5),
@@ -476,6 +514,9 @@ def bench_fp8(args, w, Q, K, V, q_tab, kv_tabs, stream):
     def timed_loop(fn):
         for _ in range(args.warmup):
             fn()
+        torch.cuda.synchronize()
+        if args.settle:
+            settle(fn, stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
@@ -663,6 +704,8 @@ def main():
     ap.add_argument("--workload", default="s32k_cp8")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--no-settle", dest="settle", action="store_false",
+                    help="skip the untimed clock-settling forwards between warm-up and the timed region")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "step_kernel_s32k_cp8_traffic.json"))
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "allgather", "fp8", "merge"), default="fwd",
                     help="fwd: the ring forward (headline); bwd: the rank's backward ring steps; allgather: "
@@ -738,7 +781,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] {w.describe()} rank {r}: warmup {args.warmup} done", file=sys.stderr, flush=True)
+    settle_n, settle_ms = settle(step, stream) if args.settle else (0, None)
+    print(f"[bench] {w.describe()} rank {r}: warmup {args.warmup} done, clocks settled after {settle_n} more "
+          f"forwards ({settle_ms} ms each)", file=sys.stderr, flush=True)
 
     # timed region: exactly K steps between two HIP events on the launch stream
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -753,6 +798,8 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
+    out_timed = out.clone()
+    lse_timed = lse.clone()
 
     # kernel-timing region: K more steps in which the library brackets every
     # step-kernel launch with two HIP events on its stream.  Kept apart from
@@ -765,8 +812,9 @@ def main():
         step()
     ek1.record(stream)
     torch.cuda.synchronize()
-    kern_ms = cp.cp_profile_read(8192)
+    kern = cp.cp_profile_read_named(8192)
     cp.cp_profile_enable(False)
+    kern_ms = [t for t, _ in kern]
     ms_per_step_instrumented = ek0.elapsed_time(ek1) / args.steps
 
     # per-forward times (median), and the forward with every staging copy run
@@ -788,14 +836,27 @@ def main():
     no_overlap_ms = statistics.median(timed_each(step_in_order, args.steps))
     props = torch.cuda.get_device_properties(dev)
 
+    # the plan the driver ran: launches per forward and the fp32 running-O
+    # round trips between them (read when merging, written when not final)
+    plan = cp.cp_ring_attn_fwd_plan(q_tab, kv_tabs)
+    launches_per_step = len(plan)
     n_launch = len(kern_ms)
-    assert n_launch > 0 and n_launch % args.steps == 0, (n_launch, args.steps)
-    launches_per_step = n_launch // args.steps  # step-kernel launches per ring forward
+    assert n_launch == launches_per_step * args.steps, (n_launch, launches_per_step, args.steps)
     avg_kernel_ms = statistics.fmean(kern_ms)
+    kernel_names = sorted(set(n for _, n in kern))
     # a ring forward's algorithmic flops spread over its launches (the launches
-    # differ in size: step 0 alone, later steps two per launch)
+    # differ in size: step 0 alone, later steps in groups)
     per_launch_flops = flops / launches_per_step
     achieved = per_launch_flops / (avg_kernel_ms * 1e-3) / 1e12
+    # algorithmic bytes of the share: Q once, K and V of every ring step once,
+    # out and LSE once; the running-O round trips and the staging copies are
+    # artefacts of the per-launch design and of the one-GPU replay, reported apart
+    rows = B * H * Sq
+    alg_bytes = rows * D * 2 + N * 2 * B * H * Skv * D * 2 + rows * D * 2 + rows * 4
+    o_chunk = B * H * L * D * 4
+    o_run_bytes = sum(o_chunk * (bool(f & cp.CP_PLAN_MERGE) + bool(f & cp.CP_PLAN_WRITE_O))
+                      for _, _, fl in plan for f in fl.values())
+    staging_bytes = sum(2 * 2 * B * H * Skv * D * 2 * cnt for first, cnt, _ in plan if first > 0)
     # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counters, only if they
     # were taken on this workload and on the kernel source that is built now
     traffic = None
@@ -809,18 +870,32 @@ def main():
         except (OSError, ValueError, KeyError):
             traffic = None
 
-    # spot check a few rows against the oracle's (outside the timed region)
-    rows = np.array([0, L - 1, L, 2 * L - 1])
-    ro, rl = cpu_baseline_rows(w, r, Q, K, V, rows)
-    eo = float(np.max(np.abs(out[0, 0, rows].float().cpu().numpy() - ro)))
-    el = float(np.max(np.abs(lse[0, 0, rows].cpu().numpy() - rl)))
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.1f} TFLOP/s; "
-          f"step kernel avg {avg_kernel_ms:.4f} ms over {n_launch} launches; spot check "
-          f"max|dout| {eo:.2e} max|dlse| {el:.2e}", file=sys.stderr, flush=True)
-
-    cpu = None
+    # parity of the timed forwards' result: every row of every (batch, head)
+    # the cpu_baseline leg computed with the oracle (all heads on a box whose
+    # host finishes them within the budget), else a few rows of head (0, 0)
+    cpu, ref = None, {}
     if args.cpu_budget > 0:
-        cpu = cpu_baseline(w, r, args.cpu_budget, Q, K, V)
+        cpu = cpu_baseline(w, r, args.cpu_budget, Q, K, V, keep=ref)
+    o_gpu = out_timed.float().cpu().numpy()
+    l_gpu = lse_timed.cpu().numpy()
+    if ref:
+        eo = max(float(np.max(np.abs(o_gpu[b, h] - ro))) for (b, h), (ro, _) in ref.items())
+        el = max(float(np.max(np.abs(l_gpu[b, h] - rl))) for (b, h), (_, rl) in ref.items())
+        checked = f"all {Sq} rows of {len(ref)} of {B * H} (batch, head) pairs"
+    else:
+        sel = np.array([0, L - 1, L, 2 * L - 1])
+        ro, rl = cpu_baseline_rows(w, r, Q, K, V, sel)
+        eo = float(np.max(np.abs(o_gpu[0, 0, sel] - ro)))
+        el = float(np.max(np.abs(l_gpu[0, 0, sel] - rl)))
+        checked = "rows 0, L-1, L, 2L-1 of head (0, 0)"
+    ok = bool(np.isfinite(o_gpu).all() and np.isfinite(l_gpu).all()) and eo <= 2e-2 and el <= 1e-3
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.1f} TFLOP/s; "
+          f"step kernel avg {avg_kernel_ms:.4f} ms over {n_launch} launches ({', '.join(kernel_names)}); "
+          f"parity on {checked}: max|dout| {eo:.2e} max|dlse| {el:.2e}", file=sys.stderr, flush=True)
+    if not ok:
+        print(f"[bench] PARITY FAILURE: max|dout| {eo:.3e} (bound 2e-2), max|dlse| {el:.3e} (bound 1e-3)",
+              file=sys.stderr, flush=True)
+        sys.exit(3)
 
     res = {
         "metric": "causal-effective attention TFLOP/s per CP-rank share; % of bf16 MFMA peak",
@@ -829,6 +904,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_forwards": settle_n,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -844,7 +920,7 @@ def main():
             "wall_s_timed": round(wall, 4),
         },
         "roofline": {
-            "kernel": "step_kernel_256<128> (QK^T, mask, online softmax, PV, fused LSE merge)",
+            "kernel": " + ".join(kernel_names) + " (QK^T, mask, online softmax, PV, fused LSE merge)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -852,23 +928,31 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "traffic_gb_per_s": (round(traffic / (avg_kernel_ms * 1e-3) / 1e9, 1) if traffic else None),
+            "alg_bytes_per_step": alg_bytes,
+            "alg_bytes_per_launch": round(alg_bytes / launches_per_step),
+            "traffic_over_alg_bytes": (round(traffic / (alg_bytes / launches_per_step), 3) if traffic else None),
+            "o_run_bytes_per_step": o_run_bytes,
+            "staging_copy_bytes_per_step": staging_bytes,
             "launches": n_launch,
             "launches_per_step": launches_per_step,
             "flop_per_launch": per_launch_flops,
             "avg_launch_ms": round(avg_kernel_ms, 5),
+            "launch_ms_first_forward": [round(t, 5) for t in kern_ms[:launches_per_step]],
             "ms_per_step_with_kernel_events": round(ms_per_step_instrumented, 5),
             "kernel_ms_per_step": round(avg_kernel_ms * launches_per_step, 5),
         },
         "timing": {
             "ms_per_step_median": round(median_ms, 5),
             "ms_per_step_no_overlap_median": round(no_overlap_ms, 5),
+            "settle_ms_last_batch": round(settle_ms, 5) if settle_ms else None,
             "note": "median over --steps forwards, each bracketed by HIP events; no_overlap runs every "
-                    "staging copy in order on the launch stream",
+                    "staging copy in order on the launch stream; the timed region starts after --warmup "
+                    "forwards and settle_forwards more, run until three batches of five agree within 1%",
         },
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count},
         "cpu_baseline": cpu,
-        "check": {"max_abs_dout": eo, "max_abs_dlse": el},
+        "check": {"max_abs_dout": eo, "max_abs_dlse": el, "rows": checked, "out_tol": 2e-2, "lse_tol": 1e-3},
     }
     print(json.dumps(res), flush=True)
 

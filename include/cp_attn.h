@@ -91,7 +91,8 @@ int cp_version(void);
  * Writes the query table of `rank` to *q_chunks and the K/V table of that
  * step's source rank to *kv_chunks (either pointer may be NULL).
  * Errors: CP_ERR_INVALID if cp_size < 1, rank or step outside [0, cp_size),
- * or chunk_len <= 0.
+ * chunk_len <= 0, or the sequence (2 * cp_size * chunk_len tokens) longer
+ * than 2^31 - 1 positions.
  */
 cp_status_t cp_zigzag_chunks(int cp_size, int rank, int chunk_len, int step,
                              cp_chunks_t* q_chunks, cp_chunks_t* kv_chunks);
@@ -142,7 +143,10 @@ cp_status_t cp_attn_step_fwd_fp8(const void* q, const void* k, const void* vt,
 
 /*
  * Standalone log-sum-exp merge of two partial results, in place on the
- * accumulator: L = ln(e^La + e^Lb), O = e^(La-L) Oa + e^(Lb-L) Ob; an
+ * accumulator ([RAF] section 3, step 5 of the RingAttention loop: combining
+ * the outputs of the chunks, which the page adds as a stated simplification;
+ * this is the exact combination for softmax attention):
+ * L = ln(e^La + e^Lb), O = e^(La-L) Oa + e^(Lb-L) Ob; an
  * operand with LSE = -inf contributes nothing; both empty gives (0, -inf).
  *   o_acc, o_part fp32 [B,H,Sq,D]; lse_acc, lse_part fp32 [B,H,Sq]
  *   out_bf16_or_null: if non-NULL, also write bf16 of the merged O.
@@ -255,6 +259,23 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream, hipStream_t copy_stream);
 
+/*
+ * The launch plan of cp_ring_attn_fwd (and cp_ring_attn_fwd_fp8) for these
+ * tables, without running anything: the loop over ring steps of [MLM]
+ * section 5 as this library groups it.  Writes the number of kernel launches
+ * to *n_launches and, for the first max_launches launches l, the first ring
+ * step it covers (first_step[l]), its number of steps (step_count[l]) and,
+ * for each query chunk c, chunk_flags[l * CP_MAX_CHUNKS + c]: 0 if the launch
+ * does not compute chunk c, else CP_PLAN_ACTIVE with CP_PLAN_MERGE (merge
+ * into the running fp32 O read from the workspace), CP_PLAN_WRITE_O (write
+ * the running O back) and CP_PLAN_FINALIZE (write out and lse).  Any output
+ * array may be NULL.  Errors: as cp_ring_attn_fwd for the tables and n_steps.
+ */
+enum { CP_PLAN_MERGE = 1, CP_PLAN_FINALIZE = 2, CP_PLAN_WRITE_O = 4, CP_PLAN_ACTIVE = 8 };
+cp_status_t cp_ring_attn_fwd_plan(const cp_chunks_t* q_chunks, const cp_chunks_t* kv_chunks_steps,
+                                  int n_steps, int max_launches, int* n_launches,
+                                  int* first_step, int* step_count, int* chunk_flags);
+
 /* Workspace bytes cp_ring_attn_fwd_fp8 needs: two staging slots of e4m3 K and
  * V^T blocks (one byte per value) for up to four ring steps, plus the fp32
  * running output [B,H,Sq,D], each rounded up to 256 bytes.  Returns 0 for
@@ -338,6 +359,26 @@ cp_status_t cp_ring_attn_bwd(const void* q, const cp_chunks_t* q_chunks,
  */
 cp_status_t cp_profile_enable(int enable);
 cp_status_t cp_profile_read(float* kernel_ms, int max_entries, int* n_entries);
+
+/* As cp_profile_read, and also writes the name of each timed kernel (the
+ * variant the launch chose, e.g. "step_kernel_256<128>"; "" for a launch
+ * with an empty grid) to kernel_names[i] when kernel_names is non-NULL.  The
+ * strings are static and owned by the library.  Either array may be NULL. */
+cp_status_t cp_profile_read_named(float* kernel_ms, const char** kernel_names,
+                                  int max_entries, int* n_entries);
+
+/*
+ * Stream-ordering test hook.  While set, the ring drivers (cp_ring_attn_fwd,
+ * cp_ring_attn_fwd_fp8, cp_ring_attn_bwd) precede every kernel launch that
+ * reads a staging slot with a bounded device-side spin of compute_us
+ * microseconds on the compute stream, and every staging copy (receive or
+ * send) with one of copy_us on the copy stream.  A launch then reads its slot
+ * late while later copies run ahead, or a copy lands late, so a missing wait
+ * in the double-buffered staging of [MLM] section 5 would change the result;
+ * with correct ordering results are bit-identical.  0 disables a side.
+ * Errors: CP_ERR_INVALID outside [0, 100000].  Process-wide setting.
+ */
+cp_status_t cp_test_set_delays(int compute_us, int copy_us);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ CP_MAX_STEPS = 64
 CP_OK, CP_ERR_INVALID, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_ERR_HIP = range(5)
 CP_STEP_WRITE, CP_STEP_MERGE = 0, 1
 CP_BWD_DQ_ACCUMULATE, CP_BWD_DKV_ACCUMULATE = 1, 2
+CP_PLAN_MERGE, CP_PLAN_FINALIZE, CP_PLAN_WRITE_O, CP_PLAN_ACTIVE = 1, 2, 4, 8
 STATUS_NAMES = {0: "CP_OK", 1: "CP_ERR_INVALID", 2: "CP_ERR_UNSUPPORTED", 3: "CP_ERR_WORKSPACE", 4: "CP_ERR_HIP"}
 
 
@@ -87,6 +88,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    i32, i32, i32, f32, vp, sz, vp, vp]),
         "cp_profile_enable": (i32, [i32]),
         "cp_profile_read": (i32, [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(ctypes.c_int)]),
+        "cp_profile_read_named": (i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), i32,
+                                        ctypes.POINTER(ctypes.c_int)]),
+        "cp_test_set_delays": (i32, [i32, i32]),
+        "cp_ring_attn_fwd_plan": (i32, [pch, pch, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -305,3 +311,31 @@ def cp_profile_read(max_entries: int = 4096):
     n = ctypes.c_int(0)
     _check(load_library().cp_profile_read(buf, max_entries, ctypes.byref(n)))
     return [buf[i] for i in range(n.value)]
+
+
+def cp_profile_read_named(max_entries: int = 4096):
+    """(milliseconds, kernel name) of every timed launch, in launch order."""
+    buf = (ctypes.c_float * max_entries)()
+    names = (ctypes.c_char_p * max_entries)()
+    n = ctypes.c_int(0)
+    _check(load_library().cp_profile_read_named(buf, names, max_entries, ctypes.byref(n)))
+    return [(buf[i], names[i].decode()) for i in range(n.value)]
+
+
+def cp_test_set_delays(compute_us: int, copy_us: int):
+    _check(load_library().cp_test_set_delays(int(compute_us), int(copy_us)))
+
+
+def cp_ring_attn_fwd_plan(q_chunks: CpChunks, kv_chunks_steps):
+    """Launches of cp_ring_attn_fwd for these tables: a list of (first_step, step_count, {chunk: flags})."""
+    n = len(kv_chunks_steps)
+    T = CpChunks * n
+    cap = CP_MAX_STEPS + 1
+    nl = ctypes.c_int(0)
+    first = (ctypes.c_int * cap)()
+    count = (ctypes.c_int * cap)()
+    flags = (ctypes.c_int * (cap * CP_MAX_CHUNKS))()
+    _check(load_library().cp_ring_attn_fwd_plan(ctypes.byref(q_chunks), T(*kv_chunks_steps), n, cap,
+                                                ctypes.byref(nl), first, count, flags))
+    return [(first[l], count[l], {c: flags[l * CP_MAX_CHUNKS + c] for c in range(CP_MAX_CHUNKS)
+                                  if flags[l * CP_MAX_CHUNKS + c]}) for l in range(nl.value)]

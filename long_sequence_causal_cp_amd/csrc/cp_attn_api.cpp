@@ -26,12 +26,23 @@
 #include "../../include/cp_attn.h"
 #include "cp_attn_internal.h"
 #include "cp_attn_fp8.h"
+#include "cp_attn_ring.h"
+#include "cp_ring_plan.h"
 
 using cpattn::StepArgs;
 
+static_assert(cpplan::kMerge == cpattn::kFlagMerge && cpplan::kFinalize == cpattn::kFlagFinalize &&
+                  cpplan::kWriteO == cpattn::kFlagWriteO,
+              "plan flags are the step kernels' flags");
+static_assert(cpplan::kMerge == CP_PLAN_MERGE && cpplan::kFinalize == CP_PLAN_FINALIZE &&
+                  cpplan::kWriteO == CP_PLAN_WRITE_O,
+              "the published plan flags are the planner's");
+
 // Most ring steps one step-kernel launch of cp_ring_attn_fwd covers; a
 // staging slot holds this many K/V blocks.
-constexpr int kStepsPerLaunch = 4;
+constexpr int kStepsPerLaunch = cpattn::kMaxStepsPerLaunch;
+// Longest delay cp_test_set_delays accepts.
+constexpr int kMaxTestDelayUs = 100000;
 
 namespace {
 
@@ -60,19 +71,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 cp_status_t check_chunks(const cp_chunks_t* t, const char* name) {
-  if (!t) return fail(CP_ERR_INVALID, "%s is NULL", name);
-  if (t->n_chunks < 1 || t->n_chunks > CP_MAX_CHUNKS)
-    return fail(CP_ERR_INVALID, "%s.n_chunks = %d, must be in [1, %d]", name, t->n_chunks, CP_MAX_CHUNKS);
-  if (t->chunk_len <= 0 || t->chunk_len % 64 != 0)
-    return fail(CP_ERR_INVALID, "%s.chunk_len = %d, must be a positive multiple of 64", name, t->chunk_len);
-  for (int i = 0; i < t->n_chunks; ++i) {
-    if (t->start[i] < 0 || t->start[i] > (int64_t)INT32_MAX - t->chunk_len)
-      return fail(CP_ERR_INVALID, "%s.start[%d] = %lld out of range [0, 2^31 - chunk_len]", name, i,
-                  (long long)t->start[i]);
-    for (int j = 0; j < i; ++j)
-      if (t->start[i] < t->start[j] + t->chunk_len && t->start[j] < t->start[i] + t->chunk_len)
-        return fail(CP_ERR_INVALID, "%s: chunks %d and %d overlap", name, j, i);
-  }
+  std::string err;
+  const cp_status_t st = cpplan::check_chunks(t, name, &err);
+  if (st != CP_OK) return fail(st, "%s", err.c_str());
   return CP_OK;
 }
 
@@ -85,23 +86,7 @@ cp_status_t check_common(int B, int H, int D, float scale) {
   return CP_OK;
 }
 
-// Visible (query, key) pairs between a query chunk starting at qs and a key
-// chunk starting at ks (key position <= query position).
-long long chunk_pairs(long long qs, long long lq, long long ks, long long lk) {
-  auto S = [lk](long long n) -> long long {  // sum_{x=1..n} min(x, lk), n >= 0
-    if (n <= 0) return 0;
-    if (n <= lk) return n * (n + 1) / 2;
-    return lk * (lk + 1) / 2 + (n - lk) * lk;
-  };
-  const long long a = qs - ks + 1, b = qs - ks + lq;
-  return S(b) - S(a - 1);
-}
-
-long long pairs_for_chunk(const cp_chunks_t* q, int c, const cp_chunks_t* kv) {
-  long long p = 0;
-  for (int j = 0; j < kv->n_chunks; ++j) p += chunk_pairs(q->start[c], q->chunk_len, kv->start[j], kv->chunk_len);
-  return p;
-}
+using cpplan::pairs_for_chunk;
 
 // Append the chunks of one [BH, Skv, D] K/V block (table `kvc`) to a launch.
 void add_kv_block(StepArgs& a, const void* k, const void* v, const cp_chunks_t* kvc) {
@@ -148,6 +133,7 @@ struct Profiler {
   std::mutex mu;
   bool enabled = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  std::vector<const char*> names;  // per used entry: the launched kernel (static string), or null
   size_t used = 0;
 };
 Profiler& profiler() {
@@ -156,11 +142,13 @@ Profiler& profiler() {
 }
 constexpr size_t kMaxTimed = 4096;
 
-// Run launch(s), bracketed by two timing events while profiling is enabled.
+// Run one kernel launch, `launch(stream, &name)`, bracketed by two timing
+// events while profiling is enabled; the name it reports is kept with them.
 template <class Launch>
 hipError_t timed(hipStream_t s, Launch&& launch) {
   Profiler& p = profiler();
-  std::pair<hipEvent_t, hipEvent_t>* slot = nullptr;
+  long slot = -1;
+  std::pair<hipEvent_t, hipEvent_t> evs{};
   {
     std::lock_guard<std::mutex> lk(p.mu);
     if (p.enabled && p.used < kMaxTimed) {
@@ -172,20 +160,29 @@ hipError_t timed(hipStream_t s, Launch&& launch) {
         e = hipEventCreateWithFlags(&e1, hipEventReleaseToDevice);
         if (e != hipSuccess) return e;
         p.ev.emplace_back(e0, e1);
+        p.names.push_back(nullptr);
       }
-      slot = &p.ev[p.used++];
+      slot = (long)p.used++;
+      evs = p.ev[slot];
     }
   }
   hipError_t e;
-  if (slot && (e = hipEventRecord(slot->first, s)) != hipSuccess) return e;
-  e = launch(s);
+  if (slot >= 0 && (e = hipEventRecord(evs.first, s)) != hipSuccess) return e;
+  const char* name = nullptr;
+  e = launch(s, &name);
   if (e != hipSuccess) return e;
-  if (slot && (e = hipEventRecord(slot->second, s)) != hipSuccess) return e;
+  if (slot >= 0) {
+    {
+      std::lock_guard<std::mutex> lk(p.mu);
+      p.names[slot] = name;
+    }
+    if ((e = hipEventRecord(evs.second, s)) != hipSuccess) return e;
+  }
   return hipSuccess;
 }
 
 hipError_t launch_step_timed(const StepArgs& a, int D, hipStream_t s) {
-  return timed(s, [&](hipStream_t st) { return cpattn::launch_step(a, D, st); });
+  return timed(s, [&](hipStream_t st, const char** nm) { return cpattn::launch_step(a, D, st, nm); });
 }
 
 // Launch arguments of the two backward kernels for one K/V block.
@@ -222,9 +219,9 @@ cpattn::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void
 
 // Both backward kernels of one block (dq rows, then dk/dv rows), each timed.
 hipError_t launch_bwd_pair(const cpattn::BwdArgs& a, hipStream_t stream) {
-  hipError_t e = timed(stream, [&](hipStream_t s) { return cpattn::launch_bwd_dq(a, s); });
+  hipError_t e = timed(stream, [&](hipStream_t s, const char** nm) { return cpattn::launch_bwd_dq(a, s, nm); });
   if (e != hipSuccess) return e;
-  return timed(stream, [&](hipStream_t s) { return cpattn::launch_bwd_dkdv(a, s); });
+  return timed(stream, [&](hipStream_t s, const char** nm) { return cpattn::launch_bwd_dkdv(a, s, nm); });
 }
 
 // ---------------- ring-driver event pool (per device) ----------------
@@ -250,6 +247,24 @@ cp_status_t get_events(int n, std::vector<hipEvent_t>& out) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// ---------------- test hook: bounded delays inside a ring replay ----------------
+// While set (cp_test_set_delays), every kernel launch of a ring driver is
+// preceded on the compute stream by a spin of compute_us microseconds, and
+// every staging copy on the copy stream by one of copy_us: a launch then
+// reads its slot late while the copies run ahead, or a copy lands late, so a
+// missing wait would change the result.
+std::mutex g_delay_mu;
+int g_delay_us[2] = {0, 0};  // [compute, copy]
+
+hipError_t test_delay(int stream_kind, hipStream_t s) {
+  int us;
+  {
+    std::lock_guard<std::mutex> lk(g_delay_mu);
+    us = g_delay_us[stream_kind];
+  }
+  return us > 0 ? cpattn::launch_delay(us, s) : hipSuccess;
+}
+
 // ---------------- ring replay shared by the bf16 and fp8 forwards ----------------
 // One launch of a ring forward: the steps it covers, the base of each step's
 // K and V block (the caller's for step 0, a staging slot after it), the query
@@ -263,114 +278,70 @@ struct RingLaunch {
   std::vector<long long> work;
 };
 
-// Launches: step 0 on the caller's block, then steps 1 .. n_steps-1 in the
-// fewest groups of at most kStepsPerLaunch steps (and at most CP_MAX_CHUNKS
-// chunks), split as evenly as possible with the smaller groups first: one
-// launch attends the query block to every staged block of its group.
-// Staging is double buffered per launch: the blocks of launch g go to slot
-// g % 2 on copy_stream while launch g-1 computes, and a later group is never
-// smaller, so its copies fit under the launch before it.  `slots` holds the
-// two slots, K blocks then V blocks (kv_bytes each, 256-byte aligned);
-// `launch(rl)` enqueues the kernel of one launch on `stream`.
+// Execute the forward ring plan (cpplan::plan_ring_fwd: step 0 on the
+// caller's block, then groups of at most `per` steps, double-buffered
+// staging slots on copy_stream).  `slots` holds the two slots, K blocks then
+// V blocks (kv_bytes each, 256-byte aligned): K slot 0 [0, per), K slot 1
+// [per, 2 per), V slot 0 [2 per, 3 per), V slot 1 [3 per, 4 per) in blocks,
+// so a slot's blocks are adjacent.  `launch(rl)` enqueues the kernel of one
+// launch on `stream`.
 template <class Launch>
 cp_status_t ring_replay(const cp_chunks_t* q_chunks, const void* const* k_steps, const void* const* v_steps,
-                        const cp_chunks_t* kv_chunks_steps, int n_steps, size_t kv_bytes, unsigned char* slots,
-                        hipStream_t stream, hipStream_t copy_stream, Launch&& launch) {
+                        const cp_chunks_t* kv_chunks_steps, int n_steps, int per, size_t kv_bytes,
+                        unsigned char* slots, hipStream_t stream, hipStream_t copy_stream, Launch&& launch) {
   cp_status_t st;
-  const int nkv = kv_chunks_steps[0].n_chunks;
-  const int per = std::max(1, std::min(kStepsPerLaunch, CP_MAX_CHUNKS / nkv));  // steps per staged launch
-  std::vector<int> l_first, l_count;  // launches: first step, number of steps
-  l_first.push_back(0);
-  l_count.push_back(1);
-  {
-    const int rest = n_steps - 1;
-    const int groups = (rest + per - 1) / per;
-    for (int g = 0, j = 1; g < groups; ++g) {
-      const int cnt = rest / groups + (g >= groups - rest % groups ? 1 : 0);
-      l_first.push_back(j);
-      l_count.push_back(cnt);
-      j += cnt;
-    }
-  }
-  const int n_launch = (int)l_first.size();
-  const int nq = q_chunks->n_chunks;
-  std::vector<std::vector<long long>> work(n_launch, std::vector<long long>(CP_MAX_CHUNKS, 0));
-  std::vector<int> first(nq, -1), last(nq, -1);
-  for (int l = 0; l < n_launch; ++l)
-    for (int c = 0; c < nq; ++c) {
-      for (int j = l_first[l]; j < l_first[l] + l_count[l]; ++j)
-        work[l][c] += pairs_for_chunk(q_chunks, c, &kv_chunks_steps[j]);
-      if (work[l][c] > 0) {
-        if (first[c] < 0) first[c] = l;
-        last[c] = l;
-      }
-    }
-  for (int c = 0; c < nq; ++c)
-    if (first[c] < 0) first[c] = last[c] = n_launch - 1;  // no key at all: write O = 0, LSE = -inf
-
-  // slots, in blocks of kv_slot bytes: K slot 0 [0, P), K slot 1 [P, 2P),
-  // V slot 0 [2P, 3P), V slot 1 [3P, 4P) with P = kStepsPerLaunch (a slot's
-  // blocks adjacent)
+  cpplan::FwdPlan plan;
+  cpplan::plan_ring_fwd(q_chunks, kv_chunks_steps, n_steps, per, &plan);
   const size_t kv_slot = round256(kv_bytes);
-  auto slot_k = [&](int g, int i) -> void* { return slots + (size_t)(kStepsPerLaunch * (g & 1) + i) * kv_slot; };
-  auto slot_v = [&](int g, int i) -> void* {
-    return slots + (size_t)(2 * kStepsPerLaunch + kStepsPerLaunch * (g & 1) + i) * kv_slot;
-  };
+  auto slot_k = [&](int slot, int i) -> void* { return slots + (size_t)(per * slot + i) * kv_slot; };
+  auto slot_v = [&](int slot, int i) -> void* { return slots + (size_t)(2 * per + per * slot + i) * kv_slot; };
 
   std::vector<hipEvent_t> ev;
-  if ((st = get_events(2 + 2 * n_launch, ev)) != CP_OK) return st;
-  hipEvent_t ev_entry = ev[0], ev_done = ev[1];
-  hipEvent_t* copied = &ev[2];              // per launch: its blocks are staged
-  hipEvent_t* released = &ev[2 + n_launch];  // per launch: done reading its slot
-
+  if ((st = get_events(plan.n_events, ev)) != CP_OK) return st;
   hipError_t e;
 #define HIP_TRY(call, what)                                   \
   do {                                                        \
     if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
   } while (0)
-
-  // copy the blocks of staged launch l (>= 1, pair slot g = l - 1) on copy_stream
-  auto stage = [&](int l) -> cp_status_t {
-    const int g = l - 1;
-    if (g >= 2) HIP_TRY(hipStreamWaitEvent(copy_stream, released[l - 2], 0), "hipStreamWaitEvent");
-    for (int i = 0; i < l_count[l]; ++i) {
-      const int j = l_first[l] + i;
-      HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k(g, i), v_steps[j], slot_v(g, i), kv_bytes, copy_stream),
-              "staging copy launch");
-    }
-    HIP_TRY(hipEventRecord(copied[l], copy_stream), "hipEventRecord");
-    return CP_OK;
-  };
-
-  HIP_TRY(hipEventRecord(ev_entry, stream), "hipEventRecord");
-  HIP_TRY(hipStreamWaitEvent(copy_stream, ev_entry, 0), "hipStreamWaitEvent");
-  for (int l = 1; l < n_launch && l <= 2; ++l)
-    if ((st = stage(l)) != CP_OK) return st;
-  for (int l = 0; l < n_launch; ++l) {
-    if (l >= 1) HIP_TRY(hipStreamWaitEvent(stream, copied[l], 0), "hipStreamWaitEvent");
-    RingLaunch rl;
-    rl.first_step = l_first[l];
-    rl.count = l_count[l];
-    for (int i = 0; i < rl.count; ++i) {
-      rl.k[i] = (l == 0) ? k_steps[0] : slot_k(l - 1, i);
-      rl.v[i] = (l == 0) ? v_steps[0] : slot_v(l - 1, i);
-    }
-    for (int c = 0; c < nq; ++c) {
-      if (l < first[c] || l > last[c] || (work[l][c] == 0 && l != last[c] && l != first[c])) continue;
-      rl.active.push_back(c);
-      rl.flags[c] = (l == first[c] ? 0 : cpattn::kFlagMerge) |
-                    (l == last[c] ? cpattn::kFlagFinalize : cpattn::kFlagWriteO);
-    }
-    rl.work = work[l];
-    HIP_TRY(launch(rl), "step kernel launch");
-    if (l + 2 < n_launch) {
-      // launch l + 2 reuses the pair slot launch l reads
-      if (l >= 1) HIP_TRY(hipEventRecord(released[l], stream), "hipEventRecord");
-      if (l + 2 >= 3 && (st = stage(l + 2)) != CP_OK) return st;
+  for (const cpplan::Op& op : plan.ops) {
+    const hipStream_t s = op.stream == cpplan::kCompute ? stream : copy_stream;
+    switch (op.kind) {
+      case cpplan::OpKind::Record:
+        HIP_TRY(hipEventRecord(ev[op.event], s), "hipEventRecord");
+        break;
+      case cpplan::OpKind::Wait:
+        HIP_TRY(hipStreamWaitEvent(s, ev[op.event], 0), "hipStreamWaitEvent");
+        break;
+      case cpplan::OpKind::Stage: {
+        const cpplan::FwdLaunch& L = plan.launches[op.index];
+        HIP_TRY(test_delay(op.stream, s), "delay kernel launch");
+        for (int i = 0; i < L.count; ++i) {
+          const int j = L.first_step + i;
+          HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k(L.slot, i), v_steps[j], slot_v(L.slot, i), kv_bytes, s),
+                  "staging copy launch");
+        }
+        break;
+      }
+      case cpplan::OpKind::Launch: {
+        const cpplan::FwdLaunch& L = plan.launches[op.index];
+        RingLaunch rl;
+        rl.first_step = L.first_step;
+        rl.count = L.count;
+        for (int i = 0; i < L.count; ++i) {
+          rl.k[i] = L.slot < 0 ? k_steps[0] : slot_k(L.slot, i);
+          rl.v[i] = L.slot < 0 ? v_steps[0] : slot_v(L.slot, i);
+        }
+        rl.active.assign(L.active, L.active + L.n_active);
+        for (int c = 0; c < CP_MAX_CHUNKS; ++c) rl.flags[c] = L.flags[c];
+        rl.work.assign(L.work, L.work + CP_MAX_CHUNKS);
+        if (op.index > 0) HIP_TRY(test_delay(op.stream, s), "delay kernel launch");
+        HIP_TRY(launch(rl), "step kernel launch");
+        break;
+      }
+      default:
+        return fail(CP_ERR_INVALID, "internal: backward operation in a forward plan");
     }
   }
-  HIP_TRY(hipEventRecord(ev_done, copy_stream), "hipEventRecord");
-  HIP_TRY(hipStreamWaitEvent(stream, ev_done, 0), "hipStreamWaitEvent");
 #undef HIP_TRY
   return CP_OK;
 }
@@ -389,15 +360,10 @@ cp_status_t cp_zigzag_chunks(int cp_size, int rank, int chunk_len, int step, cp_
   if (rank < 0 || rank >= cp_size) return fail(CP_ERR_INVALID, "rank = %d outside [0, %d)", rank, cp_size);
   if (step < 0 || step >= cp_size) return fail(CP_ERR_INVALID, "step = %d outside [0, %d)", step, cp_size);
   if (chunk_len <= 0) return fail(CP_ERR_INVALID, "chunk_len = %d must be > 0", chunk_len);
-  auto fill = [&](int r, cp_chunks_t* t) {
-    std::memset(t, 0, sizeof(*t));
-    t->n_chunks = 2;
-    t->chunk_len = chunk_len;
-    t->start[0] = (int64_t)r * chunk_len;                   // chunk r
-    t->start[1] = (int64_t)(2 * cp_size - 1 - r) * chunk_len;  // chunk 2N-1-r
-  };
-  if (q_chunks) fill(rank, q_chunks);
-  if (kv_chunks) fill(((rank - step) % cp_size + cp_size) % cp_size, kv_chunks);
+  if (2 * (int64_t)cp_size * chunk_len > (int64_t)INT32_MAX)
+    return fail(CP_ERR_INVALID, "sequence of 2 * %d chunks of %d tokens exceeds 2^31 - 1 positions", cp_size, chunk_len);
+  if (q_chunks) cpplan::zigzag_table(cp_size, rank, chunk_len, q_chunks);
+  if (kv_chunks) cpplan::zigzag_table(cp_size, ((rank - step) % cp_size + cp_size) % cp_size, chunk_len, kv_chunks);
   g_last_error.clear();
   return CP_OK;
 }
@@ -510,7 +476,7 @@ cp_status_t cp_attn_step_fwd_fp8(const void* q, const void* k, const void* vt, f
   std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return work[x] > work[y]; });
   a.n_order = (int)idx.size();
   for (int i = 0; i < a.n_order; ++i) a.order[i] = idx[i];
-  hipError_t e = timed(stream, [&](hipStream_t s) { return cpattn::launch_step_fp8(a, s); });
+  hipError_t e = timed(stream, [&](hipStream_t s, const char** nm) { return cpattn::launch_step_fp8(a, s, nm); });
   if (e != hipSuccess) return hip_fail(e, "fp8 step kernel launch");
   g_last_error.clear();
   return CP_OK;
@@ -604,20 +570,30 @@ cp_status_t cp_attn_step_bwd(const void* q, const void* k, const void* v, const 
 }
 
 size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq) {
-  if (B <= 0 || H <= 0 || Skv <= 0 || D <= 0 || Sq <= 0) return 0;
-  const size_t kv = round256((size_t)B * H * Skv * D * 2);
-  const size_t o = round256((size_t)B * H * Sq * D * 4);
-  return 4 * kStepsPerLaunch * kv + o;
+  return cpattn::ring_fwd_workspace_bytes(B, H, Skv, D, Sq, kStepsPerLaunch);
 }
 
-cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const void* const* k_steps,
-                             const void* const* v_steps, const cp_chunks_t* kv_chunks_steps, int n_steps, void* out,
-                             float* lse, int B, int H, int D, float softmax_scale, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream, hipStream_t copy_stream) {
+}  // extern "C"
+
+namespace cpattn {
+
+size_t ring_fwd_workspace_bytes(int B, int H, int Skv, int D, int Sq, int steps_per_launch) {
+  if (B <= 0 || H <= 0 || Skv <= 0 || D <= 0 || Sq <= 0 || steps_per_launch <= 0) return 0;
+  const size_t kv = round256((size_t)B * H * Skv * D * 2);
+  const size_t o = round256((size_t)B * H * Sq * D * 4);
+  return 4 * (size_t)steps_per_launch * kv + o;
+}
+
+cp_status_t ring_fwd(const void* q, const cp_chunks_t* q_chunks, const void* const* k_steps,
+                     const void* const* v_steps, const cp_chunks_t* kv_chunks_steps, int n_steps, void* out, float* lse,
+                     int B, int H, int D, float softmax_scale, void* workspace, size_t workspace_bytes,
+                     int steps_per_launch, hipStream_t stream, hipStream_t copy_stream) {
   cp_status_t st = check_common(B, H, D, softmax_scale);
   if (st != CP_OK) return st;
   if (n_steps < 1 || n_steps > CP_MAX_STEPS)
     return fail(CP_ERR_INVALID, "n_steps = %d outside [1, %d]", n_steps, CP_MAX_STEPS);
+  if (steps_per_launch < 1 || steps_per_launch > kStepsPerLaunch)
+    return fail(CP_ERR_INVALID, "internal: %d steps per launch", steps_per_launch);
   if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
   if (!k_steps || !v_steps || !kv_chunks_steps) return fail(CP_ERR_INVALID, "k_steps, v_steps, kv_chunks_steps NULL");
   for (int j = 0; j < n_steps; ++j) {
@@ -638,7 +614,7 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
     return fail(CP_ERR_INVALID, "copy_stream is NULL (pass stream itself to run the copies in order)");
   const int Sq = q_chunks->n_chunks * q_chunks->chunk_len;
   const int Skv = kv_chunks_steps[0].n_chunks * kv_chunks_steps[0].chunk_len;
-  const size_t need = cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq);
+  const size_t need = ring_fwd_workspace_bytes(B, H, Skv, D, Sq, steps_per_launch);
   if (workspace_bytes < need)
     return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   const size_t BH = (size_t)B * H;
@@ -657,8 +633,9 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
   }
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float* o_run = reinterpret_cast<float*>(ws + 4 * kStepsPerLaunch * round256(kv_bytes));
-  st = ring_replay(q_chunks, k_steps, v_steps, kv_chunks_steps, n_steps, kv_bytes, ws, stream, copy_stream,
+  float* o_run = reinterpret_cast<float*>(ws + 4 * (size_t)steps_per_launch * round256(kv_bytes));
+  st = ring_replay(q_chunks, k_steps, v_steps, kv_chunks_steps, n_steps, steps_per_launch, kv_bytes, ws, stream,
+                   copy_stream,
                    [&](const RingLaunch& rl) -> hipError_t {
                        StepArgs a;
                        base_args(a, q, rl.k[0], rl.v[0], o_run, lse, out, B, H, D, q_chunks,
@@ -671,6 +648,56 @@ cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const v
                      });
   if (st == CP_OK) g_last_error.clear();
   return st;
+}
+
+cp_status_t fail_status(cp_status_t st, const char* msg) { return fail(st, "%s", msg); }
+
+}  // namespace cpattn
+
+extern "C" {
+
+cp_status_t cp_ring_attn_fwd(const void* q, const cp_chunks_t* q_chunks, const void* const* k_steps,
+                             const void* const* v_steps, const cp_chunks_t* kv_chunks_steps, int n_steps, void* out,
+                             float* lse, int B, int H, int D, float softmax_scale, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, hipStream_t copy_stream) {
+  return cpattn::ring_fwd(q, q_chunks, k_steps, v_steps, kv_chunks_steps, n_steps, out, lse, B, H, D, softmax_scale,
+                          workspace, workspace_bytes, kStepsPerLaunch, stream, copy_stream);
+}
+
+cp_status_t cp_ring_attn_fwd_plan(const cp_chunks_t* q_chunks, const cp_chunks_t* kv_chunks_steps, int n_steps,
+                                  int max_launches, int* n_launches, int* first_step, int* step_count,
+                                  int* chunk_flags) {
+  cp_status_t st;
+  if (n_steps < 1 || n_steps > CP_MAX_STEPS)
+    return fail(CP_ERR_INVALID, "n_steps = %d outside [1, %d]", n_steps, CP_MAX_STEPS);
+  if ((st = check_chunks(q_chunks, "q_chunks")) != CP_OK) return st;
+  if (!kv_chunks_steps) return fail(CP_ERR_INVALID, "kv_chunks_steps is NULL");
+  for (int j = 0; j < n_steps; ++j) {
+    char name[48];
+    snprintf(name, sizeof(name), "kv_chunks_steps[%d]", j);
+    if ((st = check_chunks(&kv_chunks_steps[j], name)) != CP_OK) return st;
+    if (kv_chunks_steps[j].n_chunks != kv_chunks_steps[0].n_chunks ||
+        kv_chunks_steps[j].chunk_len != kv_chunks_steps[0].chunk_len)
+      return fail(CP_ERR_INVALID, "every step's K/V table must have the same n_chunks and chunk_len");
+  }
+  if (!n_launches) return fail(CP_ERR_INVALID, "n_launches is NULL");
+  cpplan::FwdPlan plan;
+  cpplan::plan_ring_fwd(q_chunks, kv_chunks_steps, n_steps, kStepsPerLaunch, &plan);
+  const int n = (int)plan.launches.size();
+  *n_launches = n;
+  for (int l = 0; l < n && l < max_launches; ++l) {
+    const cpplan::FwdLaunch& L = plan.launches[l];
+    if (first_step) first_step[l] = L.first_step;
+    if (step_count) step_count[l] = L.count;
+    if (chunk_flags)
+      for (int c = 0; c < CP_MAX_CHUNKS; ++c) {
+        bool active = false;
+        for (int i = 0; i < L.n_active; ++i) active = active || L.active[i] == c;
+        chunk_flags[l * CP_MAX_CHUNKS + c] = active ? (L.flags[c] | CP_PLAN_ACTIVE) : 0;
+      }
+  }
+  g_last_error.clear();
+  return CP_OK;
 }
 
 size_t cp_ring_attn_fwd_fp8_workspace_bytes(int B, int H, int Skv, int D, int Sq) {
@@ -735,7 +762,8 @@ cp_status_t cp_ring_attn_fwd_fp8(const void* q, const cp_chunks_t* q_chunks, con
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* o_run = reinterpret_cast<float*>(ws + 4 * kStepsPerLaunch * round256(kv_bytes));
-  st = ring_replay(q_chunks, k_steps, vt_steps, kv_chunks_steps, n_steps, kv_bytes, ws, stream, copy_stream,
+  st = ring_replay(q_chunks, k_steps, vt_steps, kv_chunks_steps, n_steps, kStepsPerLaunch, kv_bytes, ws, stream,
+                   copy_stream,
                    [&](const RingLaunch& rl) -> hipError_t {
                      cpattn::Fp8StepArgs a;
                      std::memset(&a, 0, sizeof(a));
@@ -767,7 +795,7 @@ cp_status_t cp_ring_attn_fwd_fp8(const void* q, const cp_chunks_t* q_chunks, con
                        a.order[i] = idx[i];
                        a.flags[idx[i]] = rl.flags[idx[i]];
                      }
-                     return timed(stream, [&](hipStream_t s) { return cpattn::launch_step_fp8(a, s); });
+                     return timed(stream, [&](hipStream_t s, const char** nm) { return cpattn::launch_step_fp8(a, s, nm); });
                    });
   if (st == CP_OK) g_last_error.clear();
   return st;
@@ -853,59 +881,72 @@ cp_status_t cp_ring_attn_bwd(const void* q, const cp_chunks_t* q_chunks, const v
   };
   auto adds = [&](int j) { return dkv_accumulate ? dkv_accumulate[j] != 0 : j > 0; };
 
+  cpplan::BwdPlan plan;
+  cpplan::plan_ring_bwd(n_steps, &plan);
   std::vector<hipEvent_t> ev;
-  if ((st = get_events(2 + 2 * n_steps, ev)) != CP_OK) return st;
-  hipEvent_t ev_entry = ev[0], ev_done = ev[1];
-  hipEvent_t* copied = &ev[2];              // per step: its block and partial sums are in the slot
-  hipEvent_t* computed = &ev[2 + n_steps];  // per step: its kernels are done with the slot
-
+  if ((st = get_events(plan.n_events, ev)) != CP_OK) return st;
   hipError_t e;
 #define HIP_TRY(call, what)                                   \
   do {                                                        \
     if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
   } while (0)
-  // receive of step j >= 1 on copy_stream: the block, and the partial sums it carries
-  auto receive = [&](int j) -> cp_status_t {
-    HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k(j), v_steps[j], slot_v(j), kv_bytes, copy_stream),
-            "staging copy launch");
-    if (adds(j))
-      HIP_TRY(cpattn::launch_stage_copy(dk_steps[j], slot_dk(j), dv_steps[j], slot_dv(j), g_bytes, copy_stream),
-              "staging copy launch");
-    HIP_TRY(hipEventRecord(copied[j], copy_stream), "hipEventRecord");
-    return CP_OK;
-  };
-
-  HIP_TRY(hipEventRecord(ev_entry, stream), "hipEventRecord");
-  HIP_TRY(hipStreamWaitEvent(copy_stream, ev_entry, 0), "hipStreamWaitEvent");
-  for (int j = 1; j < n_steps && j <= 2; ++j)
-    if ((st = receive(j)) != CP_OK) return st;
-  HIP_TRY(cpattn::launch_bwd_delta(static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(d_out), delta,
-                                   (int64_t)BH * Sq, D, stream),
-          "delta kernel launch");
-  for (int j = 0; j < n_steps; ++j) {
-    const int mode = (j > 0 ? CP_BWD_DQ_ACCUMULATE : 0) | (adds(j) ? CP_BWD_DKV_ACCUMULATE : 0);
-    cpattn::BwdArgs a;
-    if (j == 0) {  // the rank's own block, in place
-      a = bwd_args(q, k_steps[0], v_steps[0], d_out, lse, delta, dq, dk_steps[0], dv_steps[0], B, H, D, q_chunks,
-                   &kv_chunks_steps[0], softmax_scale, mode);
-    } else {
-      HIP_TRY(hipStreamWaitEvent(stream, copied[j], 0), "hipStreamWaitEvent");
-      a = bwd_args(q, slot_k(j), slot_v(j), d_out, lse, delta, dq, slot_dk(j), slot_dv(j), B, H, D, q_chunks,
-                   &kv_chunks_steps[j], softmax_scale, mode);
+  for (const cpplan::Op& op : plan.ops) {
+    const hipStream_t s = op.stream == cpplan::kCompute ? stream : copy_stream;
+    const int j = op.index;
+    switch (op.kind) {
+      case cpplan::OpKind::Record:
+        HIP_TRY(hipEventRecord(ev[op.event], s), "hipEventRecord");
+        break;
+      case cpplan::OpKind::Wait:
+        HIP_TRY(hipStreamWaitEvent(s, ev[op.event], 0), "hipStreamWaitEvent");
+        break;
+      case cpplan::OpKind::Receive:  // the block, and the partial sums it carries
+        HIP_TRY(test_delay(op.stream, s), "delay kernel launch");
+        HIP_TRY(cpattn::launch_stage_copy(k_steps[j], slot_k(j), v_steps[j], slot_v(j), kv_bytes, s),
+                "staging copy launch");
+        if (adds(j))
+          HIP_TRY(cpattn::launch_stage_copy(dk_steps[j], slot_dk(j), dv_steps[j], slot_dv(j), g_bytes, s),
+                  "staging copy launch");
+        break;
+      case cpplan::OpKind::Delta:
+        HIP_TRY(cpattn::launch_bwd_delta(static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(d_out),
+                                         delta, (int64_t)BH * Sq, D, s),
+                "delta kernel launch");
+        break;
+      case cpplan::OpKind::Kernels: {
+        const int mode = (j > 0 ? CP_BWD_DQ_ACCUMULATE : 0) | (adds(j) ? CP_BWD_DKV_ACCUMULATE : 0);
+        cpattn::BwdArgs a;
+        if (j == 0) {  // the rank's own block, in place
+          a = bwd_args(q, k_steps[0], v_steps[0], d_out, lse, delta, dq, dk_steps[0], dv_steps[0], B, H, D, q_chunks,
+                       &kv_chunks_steps[0], softmax_scale, mode);
+        } else {
+          HIP_TRY(test_delay(op.stream, s), "delay kernel launch");
+          a = bwd_args(q, slot_k(j), slot_v(j), d_out, lse, delta, dq, slot_dk(j), slot_dv(j), B, H, D, q_chunks,
+                       &kv_chunks_steps[j], softmax_scale, mode);
+        }
+        HIP_TRY(launch_bwd_pair(a, s), "backward kernel launch");
+        break;
+      }
+      case cpplan::OpKind::Send:  // the updated partial sums leave the slot
+        HIP_TRY(test_delay(op.stream, s), "delay kernel launch");
+        HIP_TRY(cpattn::launch_stage_copy(slot_dk(j), dk_steps[j], slot_dv(j), dv_steps[j], g_bytes, s),
+                "staging copy launch");
+        break;
+      default:
+        return fail(CP_ERR_INVALID, "internal: forward operation in a backward plan");
     }
-    HIP_TRY(launch_bwd_pair(a, stream), "backward kernel launch");
-    if (j == 0) continue;
-    // send of step j: the updated partial sums leave the slot; then the slot
-    // takes step j + 2's receive (copy_stream order keeps the two apart)
-    HIP_TRY(hipEventRecord(computed[j], stream), "hipEventRecord");
-    HIP_TRY(hipStreamWaitEvent(copy_stream, computed[j], 0), "hipStreamWaitEvent");
-    HIP_TRY(cpattn::launch_stage_copy(slot_dk(j), dk_steps[j], slot_dv(j), dv_steps[j], g_bytes, copy_stream),
-            "staging copy launch");
-    if (j + 2 < n_steps && (st = receive(j + 2)) != CP_OK) return st;
   }
-  HIP_TRY(hipEventRecord(ev_done, copy_stream), "hipEventRecord");
-  HIP_TRY(hipStreamWaitEvent(stream, ev_done, 0), "hipStreamWaitEvent");
 #undef HIP_TRY
+  g_last_error.clear();
+  return CP_OK;
+}
+
+cp_status_t cp_test_set_delays(int compute_us, int copy_us) {
+  if (compute_us < 0 || copy_us < 0 || compute_us > kMaxTestDelayUs || copy_us > kMaxTestDelayUs)
+    return fail(CP_ERR_INVALID, "delays must be in [0, %d] microseconds", kMaxTestDelayUs);
+  std::lock_guard<std::mutex> lk(g_delay_mu);
+  g_delay_us[cpplan::kCompute] = compute_us;
+  g_delay_us[cpplan::kCopy] = copy_us;
   g_last_error.clear();
   return CP_OK;
 }
@@ -918,25 +959,32 @@ cp_status_t cp_profile_enable(int enable) {
   return CP_OK;
 }
 
-cp_status_t cp_profile_read(float* kernel_ms, int max_entries, int* n_entries) {
+cp_status_t cp_profile_read_named(float* kernel_ms, const char** kernel_names, int max_entries, int* n_entries) {
   Profiler& p = profiler();
   std::lock_guard<std::mutex> lk(p.mu);
   int n = 0;
   for (size_t i = 0; i < p.used; ++i) {
     hipError_t e = hipEventSynchronize(p.ev[i].second);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-    if (kernel_ms && n < max_entries) {
-      float ms = 0.f;
-      e = hipEventElapsedTime(&ms, p.ev[i].first, p.ev[i].second);
-      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-      kernel_ms[n] = ms;
+    if (n < max_entries) {
+      if (kernel_ms) {
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, p.ev[i].first, p.ev[i].second);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        kernel_ms[n] = ms;
+      }
+      if (kernel_names) kernel_names[n] = p.names[i] ? p.names[i] : "";
+      ++n;
     }
-    if (n < max_entries) ++n;
   }
   if (n_entries) *n_entries = n;
   p.used = 0;
   g_last_error.clear();
   return CP_OK;
+}
+
+cp_status_t cp_profile_read(float* kernel_ms, int max_entries, int* n_entries) {
+  return cp_profile_read_named(kernel_ms, nullptr, max_entries, n_entries);
 }
 
 }  // extern "C"

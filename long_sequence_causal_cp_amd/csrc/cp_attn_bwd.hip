@@ -489,7 +489,7 @@ int bwd_device_cus() {
 }
 }  // namespace
 
-hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream, const char** name) {
   // The grid covers every query row of the rank, and in a ring step past the
   // first the rows of one chunk see no key (their workgroups end at once).  Where
   // a grid of 256-row workgroups holds at most one per compute unit, 128-row
@@ -499,25 +499,29 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   int bm = bwd_dq_rows(a.q_chunk_len);
   if (bm == 256 && (long long)a.BH * (a.Sq / 256) <= bwd_device_cus()) bm = 128;
   const long long grid = (long long)a.BH * (a.Sq / bm);
+  if (name) *name = nullptr;
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk((unsigned)(2 * bm));  // one wave per 32 rows
+  const char* n;
   if (a.D == 128) {
-    if (bm == 256) hipLaunchKernelGGL((bwd_dq_kernel<128, 8>), g, blk, 0, stream, a);
-    else if (bm == 128) hipLaunchKernelGGL((bwd_dq_kernel<128, 4>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<128, 2>), g, blk, 0, stream, a);
+    if (bm == 256) { hipLaunchKernelGGL((bwd_dq_kernel<128, 8>), g, blk, 0, stream, a); n = "bwd_dq_kernel<128, 8>"; }
+    else if (bm == 128) { hipLaunchKernelGGL((bwd_dq_kernel<128, 4>), g, blk, 0, stream, a); n = "bwd_dq_kernel<128, 4>"; }
+    else { hipLaunchKernelGGL((bwd_dq_kernel<128, 2>), g, blk, 0, stream, a); n = "bwd_dq_kernel<128, 2>"; }
   } else {
-    if (bm == 256) hipLaunchKernelGGL((bwd_dq_kernel<64, 8>), g, blk, 0, stream, a);
-    else if (bm == 128) hipLaunchKernelGGL((bwd_dq_kernel<64, 4>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<64, 2>), g, blk, 0, stream, a);
+    if (bm == 256) { hipLaunchKernelGGL((bwd_dq_kernel<64, 8>), g, blk, 0, stream, a); n = "bwd_dq_kernel<64, 8>"; }
+    else if (bm == 128) { hipLaunchKernelGGL((bwd_dq_kernel<64, 4>), g, blk, 0, stream, a); n = "bwd_dq_kernel<64, 4>"; }
+    else { hipLaunchKernelGGL((bwd_dq_kernel<64, 2>), g, blk, 0, stream, a); n = "bwd_dq_kernel<64, 2>"; }
   }
+  if (name) *name = n;
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  // As for the forward: a grid of 256-key workgroups with exactly one per
-  // compute unit, in a step that holds a diagonal chunk pair, has blocks whose
-  // work ranges from a few query tiles to twice the mean; 128-key blocks, two
-  // per unit, let the light ones finish beside the heavy ones.  A key's dK, dV
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** name) {
+  // In a step that holds a diagonal chunk pair, a grid of 256-key workgroups
+  // with at most one per compute unit has blocks whose work ranges from a few
+  // query tiles to twice the mean, and with fewer blocks than units it also
+  // leaves units idle; 128-key blocks, two per unit, let the light ones finish
+  // beside the heavy ones and spread the work over more units.  A key's dK, dV
   // are the same either way (its wave sums the same query tiles in order).
   int bn = bwd_dkdv_keys(a.kv_chunk_len);
   bool diag = false;
@@ -525,17 +529,20 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
     for (int k = 0; k < a.n_kv_chunks; ++k) diag = diag || a.q_start[i] == a.kv_start[k];
   if (bn == 256 && diag && (long long)a.BH * (a.Skv / 256) <= bwd_device_cus()) bn = 128;
   const long long grid = (long long)a.BH * (a.Skv / bn);
+  if (name) *name = nullptr;
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk((unsigned)(2 * bn));  // one wave per 32 keys
+  const char* n;
   if (a.D == 128) {
-    if (bn == 256) hipLaunchKernelGGL((bwd_dkdv_kernel<128, 8>), g, blk, 0, stream, a);
-    else if (bn == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128, 4>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<128, 2>), g, blk, 0, stream, a);
+    if (bn == 256) { hipLaunchKernelGGL((bwd_dkdv_kernel<128, 8>), g, blk, 0, stream, a); n = "bwd_dkdv_kernel<128, 8>"; }
+    else if (bn == 128) { hipLaunchKernelGGL((bwd_dkdv_kernel<128, 4>), g, blk, 0, stream, a); n = "bwd_dkdv_kernel<128, 4>"; }
+    else { hipLaunchKernelGGL((bwd_dkdv_kernel<128, 2>), g, blk, 0, stream, a); n = "bwd_dkdv_kernel<128, 2>"; }
   } else {
-    if (bn == 256) hipLaunchKernelGGL((bwd_dkdv_kernel<64, 8>), g, blk, 0, stream, a);
-    else if (bn == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<64, 4>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<64, 2>), g, blk, 0, stream, a);
+    if (bn == 256) { hipLaunchKernelGGL((bwd_dkdv_kernel<64, 8>), g, blk, 0, stream, a); n = "bwd_dkdv_kernel<64, 8>"; }
+    else if (bn == 128) { hipLaunchKernelGGL((bwd_dkdv_kernel<64, 4>), g, blk, 0, stream, a); n = "bwd_dkdv_kernel<64, 4>"; }
+    else { hipLaunchKernelGGL((bwd_dkdv_kernel<64, 2>), g, blk, 0, stream, a); n = "bwd_dkdv_kernel<64, 2>"; }
   }
+  if (name) *name = n;
   return hipGetLastError();
 }
 

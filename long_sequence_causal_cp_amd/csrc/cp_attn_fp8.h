@@ -41,6 +41,8 @@ struct Fp8StepArgs {
 constexpr int kFp8BlockRows = 256;
 constexpr int kFp8RowQuantum = 128;
 
-hipError_t launch_step_fp8(const Fp8StepArgs& a, hipStream_t stream);
+// *name (if name is non-null) receives the launched kernel's name, or null
+// when the grid is empty.
+hipError_t launch_step_fp8(const Fp8StepArgs& a, hipStream_t stream, const char** name = nullptr);
 
 }  // namespace cpattn

@@ -473,7 +473,7 @@ int fp8_device_cus() {
 
 }  // namespace
 
-hipError_t launch_step_fp8(const Fp8StepArgs& args, hipStream_t stream) {
+hipError_t launch_step_fp8(const Fp8StepArgs& args, hipStream_t stream, const char** name) {
   // A row's result does not depend on the row-block size (a block only decides
   // which tiles it stages; keys past a row are masked), so the launch picks it:
   // 256-row blocks unless their grid would leave compute units idle, or would
@@ -489,11 +489,13 @@ hipError_t launch_step_fp8(const Fp8StepArgs& args, hipStream_t stream) {
   if (bm == 256 && (g256 < fp8_device_cus() || (diag && g256 <= fp8_device_cus()))) bm = 128;
   a.rb_per_chunk = a.q_chunk_len / bm;
   const long long grid = (long long)a.n_order * a.rb_per_chunk * a.BH;
+  if (name) *name = nullptr;
   if (grid <= 0) return hipSuccess;
   if (bm == 256)
     hipLaunchKernelGGL(fp8_step_kernel, dim3((unsigned)grid), dim3(512), 0, stream, a);
   else
     hipLaunchKernelGGL(fp8_step_kernel_128, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  if (name) *name = bm == 256 ? "fp8_step_kernel" : "fp8_step_kernel_128";
   return hipGetLastError();
 }
 

@@ -71,8 +71,10 @@ struct BwdArgs {
 // key-stationary dk/dv kernel (rows and keys per workgroup for a chunk length).
 int bwd_dq_rows(int q_chunk_len);
 int bwd_dkdv_keys(int kv_chunk_len);
-hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+// *name (if name is non-null) receives the launched kernel's name, or null
+// when the grid is empty; the same holds for launch_step.
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream, const char** name = nullptr);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** name = nullptr);
 // delta[r] = sum_d dout[r][d] * out[r][d] over `rows` rows of D bf16 values.
 hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, float* delta, int64_t rows, int D,
                             hipStream_t stream);
@@ -81,12 +83,16 @@ hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, float* de
 int step_block_rows(int q_chunk_len);
 
 // Launch the step kernel; `grid` = n_order * rb_per_chunk * BH workgroups.
-hipError_t launch_step(const StepArgs& a, int D, hipStream_t stream);
+hipError_t launch_step(const StepArgs& a, int D, hipStream_t stream, const char** name = nullptr);
 
 // Copy one ring step's K and V blocks (`bytes` each, a multiple of 16) into a
 // staging slot on `stream` (the copy stream of the ring driver).
 hipError_t launch_stage_copy(const void* k_src, void* k_dst, const void* v_src, void* v_dst, size_t bytes,
                              hipStream_t stream);
+
+// A single-wave spin of `us` microseconds of the device's constant-rate
+// clock on `stream` (stream-ordering tests only); it always ends.
+hipError_t launch_delay(int us, hipStream_t stream);
 
 // Standalone merge kernel.
 hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,

@@ -1,8 +1,9 @@
 """Shared plumbing for the GPU parity tests: rank buffers, ring calls, oracle rows.
 
-Rank buffers are gathered from the full sequence with the library's own
-chunk tables (cp_zigzag_chunks); expected values come from the fp64 oracle
-with its own index maths.  The oracle runs per (batch, head) in a thread
+Zigzag chunk tables are built from the oracle's index maths
+(oracle.local_positions, oracle.ring_kv_positions) and checked equal to the
+library's cp_zigzag_chunks before use; rank buffers are gathered from the
+full sequence with them, and expected values come from the fp64 oracle.  The oracle runs per (batch, head) in a thread
 pool (numpy releases the GIL in matmul and exp), at most 16 threads.
 """
 from __future__ import annotations
@@ -33,9 +34,26 @@ def gather(x, table, dev):
     return x.index_select(2, idx).contiguous().to(dev)
 
 
+def table_from_positions(pos, chunk_len):
+    """Chunk table of a local buffer whose rows sit at absolute positions ``pos`` (whole chunks)."""
+    pos = np.asarray(pos, np.int64)
+    assert len(pos) % chunk_len == 0
+    starts = [int(s) for s in pos[::chunk_len]]
+    for i, s in enumerate(starts):
+        assert np.array_equal(pos[i * chunk_len:(i + 1) * chunk_len], np.arange(s, s + chunk_len))
+    return cp.CpChunks.make(starts, chunk_len)
+
+
 def zigzag_tables(cp_size, rank, L):
-    q_tab = cp.cp_zigzag_chunks(cp_size, rank, L, 0)[0]
-    kv = [cp.cp_zigzag_chunks(cp_size, rank, L, j)[1] for j in range(cp_size)]
+    """The rank's query table and the K/V table of every ring step, from the oracle's positions; the
+    library's cp_zigzag_chunks must give the same tables."""
+    S = 2 * cp_size * L
+    q_tab = table_from_positions(oracle.local_positions(S, cp_size, rank), L)
+    kv = [table_from_positions(oracle.ring_kv_positions(S, cp_size, rank, j), L) for j in range(cp_size)]
+    for j in range(cp_size):
+        lq, lkv = cp.cp_zigzag_chunks(cp_size, rank, L, j)
+        assert (lq.starts(), lq.chunk_len) == (q_tab.starts(), L), (cp_size, rank, j)
+        assert (lkv.starts(), lkv.chunk_len) == (kv[j].starts(), L), (cp_size, rank, j)
     return q_tab, kv
 
 

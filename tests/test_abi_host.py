@@ -289,3 +289,37 @@ def test_ring_fwd_fp8_validation(lib):
     assert call(ws=need - 1) == cb.CP_ERR_WORKSPACE
     assert call(vscale=-1.0) == cb.CP_ERR_INVALID
     assert cb.cp_last_error()
+
+
+def test_test_delay_hook_validation(lib):
+    for bad in ((-1, 0), (0, -1), (100001, 0), (0, 10 ** 6)):
+        assert lib.cp_test_set_delays(*bad) == cb.CP_ERR_INVALID
+        assert cb.cp_last_error()
+    assert lib.cp_test_set_delays(0, 0) == cb.CP_OK
+
+
+def test_zigzag_rejects_sequences_past_int32(lib):
+    # chunk tables hold positions below 2^31 - 1 (start + chunk_len <= 2^31 - 1)
+    for n, L in ((1 << 16, 1 << 15), (1 << 14, 1 << 16)):      # 2^32 and 2^31 positions
+        with pytest.raises(cb.CpError):
+            cb.cp_zigzag_chunks(n, 0, L, 0)
+    n, L = 1 << 14, (1 << 16) - 1                               # 2^31 - 2^15 positions
+    q, _ = cb.cp_zigzag_chunks(n, n - 1, L, 0)
+    assert q.starts() == [(n - 1) * L, n * L]
+
+
+def test_profile_read_named_when_empty(lib):
+    assert cb.cp_profile_read_named() == []
+
+
+def test_ring_plan_query(lib):
+    """The published plan of the 32K cp=8 share, rank 0: step 0 alone, then steps 1-3 and 4-7; chunk 0
+    (positions 0..2047) sees only its own block and finishes at step 0; chunk 15 is written at step 0,
+    merged in both groups and finalised by the last."""
+    q, _ = cb.cp_zigzag_chunks(8, 0, 2048, 0)
+    kv = [cb.cp_zigzag_chunks(8, 0, 2048, j)[1] for j in range(8)]
+    A, M, W, F = cb.CP_PLAN_ACTIVE, cb.CP_PLAN_MERGE, cb.CP_PLAN_WRITE_O, cb.CP_PLAN_FINALIZE
+    assert cb.cp_ring_attn_fwd_plan(q, kv) == [(0, 1, {0: A | F, 1: A | W}), (1, 3, {1: A | M | W}),
+                                               (4, 4, {1: A | M | F})]
+    with pytest.raises(cb.CpError):
+        cb.cp_ring_attn_fwd_plan(q, [])

@@ -17,9 +17,10 @@ def test_e4m3_rounding_is_round_to_nearest_with_three_mantissa_bits():
 
 
 def test_fp8_error_model_within_tolerance():
-    """The fp8 step's output tolerance (0.1) rests on the e4m3 rounding of the
-    probabilities; the fp64 model of that rounding stays below half of it on
-    the workloads the fp8 GPU test uses."""
+    """The fp8 step's output tolerance is derived from the e4m3 rounding of the
+    probabilities (1.5 times this model's deviation on the compared rows); the
+    model's deviation is nonzero and stays below 0.05 on the workloads the fp8
+    GPU test uses."""
     import numpy as np
     import workloads
     from fp8_helpers import dequantize, emulated_error, quantize

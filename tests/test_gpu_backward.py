@@ -169,7 +169,10 @@ def test_step_bwd_zigzag(name, H, ranks, steps):
 @pytest.mark.parametrize("D,L,B,H", [(128, 64, 1, 2), (64, 128, 2, 3), (64, 64, 1, 8), (128, 192, 1, 2),
                                      (128, 256, 2, 4), (64, 256, 1, 2)])
 def test_bwd_kernel_variants(D, L, B, H):
-    """Every compiled dq (64/128/256 rows) and dk/dv (64/128 keys) variant, both head-to-XCD mappings."""
+    """The dq kernel at 64 and 128 rows and the dk/dv kernel at 64, 128 and 256 keys (256 only off the
+    diagonal step), both head-to-XCD mappings.  With B*H*Sq/256 at most the compute-unit count the launch
+    takes 128-row dq blocks for every 256-multiple chunk, and 128-key dk/dv blocks on diagonal steps; the
+    256-row dq and diagonal 256-key dk/dv blocks are covered by test_bwd_grids_above_cu_count."""
     N = 3
     S = 2 * N * L
     Q, K, V = workloads.make_qkv_scaled((B, H, S, D), 3 * D + L)
@@ -181,6 +184,28 @@ def test_bwd_kernel_variants(D, L, B, H):
         for j in range(N):
             _announce("variant", D, L, B, H, "rank", r, "step", j)
             check_step(Q, K, V, dO, q_tab, kv_tabs[j], 1 / math.sqrt(D), fwd=fwd)
+
+
+def test_bwd_grids_above_cu_count():
+    """72 heads of 1024 local rows: B*H*Sq/256 = 288 exceeds the 256 compute units, so the launches take
+    256-row dq blocks and, on the diagonal step 0, 256-key dk/dv blocks (the forms of the 32K cp=8
+    share's backward); every rank and step against the oracle on all heads."""
+    N, L, D, H = 2, 512, 128, 72
+    S = 2 * N * L
+    assert H * 2 * L // 256 > torch.cuda.get_device_properties(DEV).multi_processor_count
+    Q, K, V = workloads.make_qkv_scaled((1, H, S, D), 909)
+    gen = torch.Generator().manual_seed(910)
+    dO = torch.randn(1, H, S, D, generator=gen).to(torch.bfloat16)
+    for r in range(N):
+        q_tab, kv_tabs = zigzag_tables(N, r, L)
+        fwd = forward_rows(Q, K, V, positions(q_tab), 1 / math.sqrt(D))
+        for j in range(N):
+            _announce("grid above CUs", "H", H, "rank", r, "step", j)
+            cp.cp_profile_enable(True)
+            check_step(Q, K, V, dO, q_tab, kv_tabs[j], 1 / math.sqrt(D), fwd=fwd)
+            names = [n for _, n in cp.cp_profile_read_named()]
+            cp.cp_profile_enable(False)
+            assert names == ["bwd_dq_kernel<128, 8>", "bwd_dkdv_kernel<128, 8>"], names
 
 
 @pytest.mark.parametrize("qs,ks", [(3.0, 3.0), (0.2, 6.0)])

@@ -5,13 +5,13 @@ Q, K and V are quantised to e4m3 with power-of-two per-tensor scales
 A rank's share is computed as the ring's chain of steps: step 0 writes,
 later steps merge, the last one also writes the bf16 output.
 
-Tolerance: max-abs 0.1 on the output and 1e-3 on the natural-log LSE.  The
-output bound comes from the arithmetic: rounding the probabilities to e4m3
-(relative 2^-4) before the PV product, modelled in fp64 by
-fp8_helpers.emulated_error, moves the output by at most 0.035-0.039 on these
-workloads (test_fp8_error_model_within_tolerance pins that below 0.05), and
-the bf16 output adds at most 2^-9 of |out|.  The LSE is formed from fp32 sums
-of the unrounded probabilities of exact fp8 products, as in the bf16 path.
+Tolerance: 1e-3 on the natural-log LSE, and on the output, per case,
+1.5 times the deviation that rounding the probabilities to e4m3 (relative
+2^-4) before the PV product causes on the compared rows, modelled in fp64 by
+fp8_helpers.emulated_error (0.035-0.039 on the zigzag workloads;
+test_fp8_error_model_within_tolerance pins that below 0.05), plus 2^-8 of
+max |out| for the bf16 output.  The LSE is formed from fp32 sums of the
+unrounded probabilities of exact fp8 products, as in the bf16 path.
 """
 import numpy as np
 import pytest
@@ -25,7 +25,6 @@ from gpu_helpers import positions, zigzag_tables
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-OUT_TOL_FP8 = 0.1
 LSE_TOL = 1e-3
 
 
@@ -56,6 +55,25 @@ def _ring_fp8(qc, kc, vc, sq, sk, sv, q_tab, kv_tabs, scale):
     return out, lse
 
 
+def _compare_rows(out, lse, Qd, Kd, Vd, sel, local, H, scale):
+    """Max-abs output and LSE errors of batch 0, heads 0..H-1, local rows `local` (absolute positions
+    `sel`) against the oracle on dequantised values, and the output bound from the e4m3 model on those
+    rows."""
+    eo = el = em = amax = 0.0
+    kmax = int(sel.max()) + 1
+    for h in range(H):
+        q, k, v = Qd[0, h].numpy()[sel], Kd[0, h, :kmax].numpy(), Vd[0, h, :kmax].numpy()
+        ro, rl = oracle.masked_attention(q, sel, k, v, np.arange(kmax), scale)
+        eo = max(eo, float(np.max(np.abs(out[0, h, local].float().cpu().numpy() - ro))))
+        el = max(el, float(np.max(np.abs(lse[0, h, local].cpu().numpy() - rl))))
+        em = max(em, emulated_error(q, k, v, sel, scale))
+        amax = max(amax, float(np.max(np.abs(ro))))
+    tol = out_tolerance(em, amax)
+    print(f"  max|dout| = {eo:.3e} (model {em:.3e}, ratio {eo / max(em, 1e-30):.2f}, bound {tol:.3e})  "
+          f"max|dlse| = {el:.3e}", flush=True)
+    return eo, el, tol
+
+
 @pytest.mark.parametrize("name,H,ranks,rows", [("s8k_cp2", 2, (0, 1), None), ("s16k_cp4", 2, (1, 2), 256),
                                                ("s32k_cp8", 2, (0, 7), 128)])
 def test_fp8_ring_share_matches_oracle(name, H, ranks, rows):
@@ -71,16 +89,8 @@ def test_fp8_ring_share_matches_oracle(name, H, ranks, rows):
         n = len(qpos)
         local = np.arange(n) if rows is None else np.unique(np.concatenate(
             [np.random.default_rng(r).choice(n, rows, replace=False), [0, 1, w.chunk_len - 1, w.chunk_len, n - 1]]))
-        eo = el = 0.0
-        for h in range(H):
-            sel = qpos[local]
-            kmax = int(sel.max()) + 1
-            ro, rl = oracle.masked_attention(Qd[0, h].numpy()[sel], sel, Kd[0, h, :kmax].numpy(),
-                                             Vd[0, h, :kmax].numpy(), np.arange(kmax), w.scale)
-            eo = max(eo, float(np.max(np.abs(out[0, h, local].float().cpu().numpy() - ro))))
-            el = max(el, float(np.max(np.abs(lse[0, h, local].cpu().numpy() - rl))))
-        print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
-        assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)
+        eo, el, tol = _compare_rows(out, lse, Qd, Kd, Vd, qpos[local], local, H, w.scale)
+        assert eo <= tol and el <= LSE_TOL, (eo, tol, el)
 
 
 @pytest.mark.parametrize("name,H,ranks,rows", [("s8k_cp2", 2, (0, 1), None), ("s32k_cp8", 2, (0, 7), 128)])
@@ -115,16 +125,8 @@ def test_fp8_ring_driver_matches_oracle(name, H, ranks, rows):
         n = len(qpos)
         local = np.arange(n) if rows is None else np.unique(np.concatenate(
             [np.random.default_rng(r).choice(n, rows, replace=False), [0, 1, w.chunk_len - 1, w.chunk_len, n - 1]]))
-        eo = el = 0.0
-        for h in range(H):
-            sel = qpos[local]
-            kmax = int(sel.max()) + 1
-            ro, rl = oracle.masked_attention(Qd[0, h].numpy()[sel], sel, Kd[0, h, :kmax].numpy(),
-                                             Vd[0, h, :kmax].numpy(), np.arange(kmax), w.scale)
-            eo = max(eo, float(np.max(np.abs(out[0, h, local].float().cpu().numpy() - ro))))
-            el = max(el, float(np.max(np.abs(lse[0, h, local].cpu().numpy() - rl))))
-        print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
-        assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)
+        eo, el, tol = _compare_rows(out, lse, Qd, Kd, Vd, qpos[local], local, H, w.scale)
+        assert eo <= tol and el <= LSE_TOL, (eo, tol, el)
 
 
 @pytest.mark.parametrize("H", [2, 256])
@@ -169,7 +171,7 @@ def _check_fp8_step(q_tab, kv_tab, H, D, seed):
     cp.cp_attn_step_fwd_fp8(q, k, vt, o, lse, out, q_tab, kv_tab, scale, sq, sk, sv, cp.CP_STEP_WRITE)
     torch.cuda.synchronize()
     out_h, lse_h = out.float().cpu().numpy(), lse.cpu().numpy()
-    eo = el = em = 0.0
+    eo = el = em = amax = 0.0
     for h in range(H):
         ro, rl = oracle.masked_attention(Qd[0, h][qpos], qpos, Kd[0, h][kpos], Vd[0, h][kpos], kpos, scale)
         empty = np.isinf(rl)
@@ -178,8 +180,10 @@ def _check_fp8_step(q_tab, kv_tab, H, D, seed):
         eo = max(eo, float(np.max(np.abs(out_h[0, h][~empty] - ro[~empty]))))
         el = max(el, float(np.max(np.abs(lse_h[0, h][~empty] - rl[~empty]))))
         em = max(em, emulated_error(Qd[0, h][qpos], Kd[0, h][kpos], Vd[0, h][kpos], qpos, scale, kpos))
-    tol = out_tolerance(em, OUT_TOL_FP8)
-    print(f"  max|dout| = {eo:.3e} (model {em:.3e}, bound {tol:.3e})  max|dlse| = {el:.3e}", flush=True)
+        amax = max(amax, float(np.max(np.abs(ro[~empty]))))
+    tol = out_tolerance(em, amax)
+    print(f"  max|dout| = {eo:.3e} (model {em:.3e}, ratio {eo / max(em, 1e-30):.2f}, bound {tol:.3e})  "
+          f"max|dlse| = {el:.3e}", flush=True)
     assert eo <= tol and el <= LSE_TOL, (eo, tol, el)
 
 
@@ -211,7 +215,7 @@ def test_fp8_ring_batch_heads_xcd_mapping(rank, L):
     torch.cuda.synchronize()
     qpos = positions(q_tab)
     out_h, lse_h = out.float().cpu().numpy(), lse.cpu().numpy()
-    eo = el = em = 0.0
+    eo = el = em = amax = 0.0
     for b in range(B):
         for h in range(H):
             kmax = int(qpos.max()) + 1
@@ -220,8 +224,10 @@ def test_fp8_ring_batch_heads_xcd_mapping(rank, L):
             eo = max(eo, float(np.max(np.abs(out_h[b, h] - ro))))
             el = max(el, float(np.max(np.abs(lse_h[b, h] - rl))))
             em = max(em, emulated_error(Qd[b, h][qpos], Kd[b, h, :kmax], Vd[b, h, :kmax], qpos, scale))
-    tol = out_tolerance(em, OUT_TOL_FP8)
-    print(f"  max|dout| = {eo:.3e} (model {em:.3e}, bound {tol:.3e})  max|dlse| = {el:.3e}", flush=True)
+            amax = max(amax, float(np.max(np.abs(ro))))
+    tol = out_tolerance(em, amax)
+    print(f"  max|dout| = {eo:.3e} (model {em:.3e}, ratio {eo / max(em, 1e-30):.2f}, bound {tol:.3e})  "
+          f"max|dlse| = {el:.3e}", flush=True)
     assert eo <= tol and el <= LSE_TOL, (eo, tol, el)
 
 
@@ -252,7 +258,7 @@ def test_fp8_ring_full_share_256_row_blocks():
                                       [0, 1, L - 1, L, 2 * L - 1]]))
     sel = qpos[local]
     kmax = int(sel.max()) + 1
-    eo = el = 0.0
+    eo = el = em = amax = 0.0
     for h in (0, 17, 31):
         qd = dequantize(qc[0, h], sq)
         kd = dequantize(kc[0, h, :kmax], sk)
@@ -260,5 +266,9 @@ def test_fp8_ring_full_share_256_row_blocks():
         ro, rl = oracle.masked_attention(qd[sel], sel, kd, vd, np.arange(kmax), w.scale)
         eo = max(eo, float(np.max(np.abs(out[0, h, local].float().cpu().numpy() - ro))))
         el = max(el, float(np.max(np.abs(lse[0, h, local].cpu().numpy() - rl))))
-    print(f"  max|dout| = {eo:.3e}  max|dlse| = {el:.3e}", flush=True)
-    assert eo <= OUT_TOL_FP8 and el <= LSE_TOL, (eo, el)
+        em = max(em, emulated_error(qd[sel], kd, vd, sel, w.scale))
+        amax = max(amax, float(np.max(np.abs(ro))))
+    tol = out_tolerance(em, amax)
+    print(f"  max|dout| = {eo:.3e} (model {em:.3e}, ratio {eo / max(em, 1e-30):.2f}, bound {tol:.3e})  "
+          f"max|dlse| = {el:.3e}", flush=True)
+    assert eo <= tol and el <= LSE_TOL, (eo, tol, el)
