@@ -276,6 +276,32 @@ cp_status_t cp_ring_attn_fwd_plan(const cp_chunks_t* q_chunks, const cp_chunks_t
                                   int n_steps, int max_launches, int* n_launches,
                                   int* first_step, int* step_count, int* chunk_flags);
 
+/*
+ * cp_ring_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The staging slots and the fp32 running
+ * output live in a static array of the library on each device
+ * (cp_ring_attn_fwd_noalloc_max_bytes() bytes, 64 MiB, held from the library's
+ * load until the process ends); nothing is allocated.  The launch grouping
+ * is cp_ring_attn_fwd's (up to four ring steps per launch) when its slots fit
+ * the array, else fewer steps per launch; the results then differ from
+ * cp_ring_attn_fwd's only by rounding order.
+ * Arguments, errors and stream semantics: as cp_ring_attn_fwd.  A share whose
+ * slots for one ring step per launch plus running output exceed the array is
+ * refused with CP_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one device uses that device's single array: calls that
+ * overlap in time on one device (other streams, other host threads) race and
+ * must be serialised by the caller.  No part of the array needs clearing
+ * between calls (every byte read is written earlier in the same call).
+ */
+size_t cp_ring_attn_fwd_noalloc_max_bytes(void);
+cp_status_t cp_ring_attn_fwd_noalloc(const void* q, const cp_chunks_t* q_chunks,
+                                     const void* const* k_steps, const void* const* v_steps,
+                                     const cp_chunks_t* kv_chunks_steps, int n_steps,
+                                     void* out, float* lse,
+                                     int B, int H, int D, float softmax_scale,
+                                     hipStream_t stream, hipStream_t copy_stream);
+
 /* Workspace bytes cp_ring_attn_fwd_fp8 needs: two staging slots of e4m3 K and
  * V^T blocks (one byte per value) for up to four ring steps, plus the fp32
  * running output [B,H,Sq,D], each rounded up to 256 bytes.  Returns 0 for

@@ -91,6 +91,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "cp_profile_read_named": (i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), i32,
                                         ctypes.POINTER(ctypes.c_int)]),
         "cp_test_set_delays": (i32, [i32, i32]),
+        "cp_ring_attn_fwd_noalloc_max_bytes": (sz, []),
+        "cp_ring_attn_fwd_noalloc": (i32, [vp, pch, ctypes.POINTER(vp), ctypes.POINTER(vp), pch, i32, vp, vp,
+                                           i32, i32, i32, f32, vp, vp]),
         "cp_ring_attn_fwd_plan": (i32, [pch, pch, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                         ctypes.POINTER(i32), ctypes.POINTER(i32)]),
     }
@@ -236,6 +239,29 @@ def cp_ring_attn_fwd(q, q_chunks: CpChunks, k_steps, v_steps, kv_chunks_steps, o
                                            _ptr(out), _ptr(lse), B, H, D, float(softmax_scale),
                                            _ptr(workspace), workspace.numel(), _stream(stream),
                                            _stream(copy_stream)))
+
+
+def cp_ring_attn_fwd_noalloc(q, q_chunks: CpChunks, k_steps, v_steps, kv_chunks_steps, out, lse,
+                             softmax_scale: float, stream=None, copy_stream=None):
+    """cp_ring_attn_fwd with the library's static scratch array as its workspace (no allocation)."""
+    import torch
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    _need(lse, torch.float32, "lse")
+    n = len(k_steps)
+    if len(v_steps) != n or len(kv_chunks_steps) != n:
+        raise ValueError("k_steps, v_steps and kv_chunks_steps must have the same length")
+    for t in list(k_steps) + list(v_steps):
+        _need(t, torch.bfloat16, "k/v step")
+    kp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in k_steps])
+    vp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in v_steps])
+    tables = (CpChunks * max(n, 1))(*kv_chunks_steps)
+    if copy_stream is None:
+        raise ValueError("copy_stream is required (a torch.cuda.Stream; stream itself runs the copies in order)")
+    B, H, _, D = q.shape
+    _check(load_library().cp_ring_attn_fwd_noalloc(_ptr(q), ctypes.byref(q_chunks), kp, vp, tables, n,
+                                                   _ptr(out), _ptr(lse), B, H, D, float(softmax_scale),
+                                                   _stream(stream), _stream(copy_stream)))
 
 
 def cp_ring_attn_fwd_fp8_workspace_bytes(B: int, H: int, Skv: int, D: int, Sq: int) -> int:

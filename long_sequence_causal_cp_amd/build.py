@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libcp_attn.so")
 
-SOURCES = ["cp_attn_kernels.hip", "cp_attn_bwd.hip", "cp_attn_fp8.hip", "cp_ring_plan.cpp", "cp_attn_api.cpp"]
+SOURCES = ["cp_attn_kernels.hip", "cp_attn_bwd.hip", "cp_attn_fp8.hip", "cp_ring_plan.cpp", "cp_attn_api.cpp",
+           "cp_attn_noalloc.hip"]
 CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")  # measurement tool, its own executable
 CEILING_BIN = os.path.join(HERE, "mfma_ceiling")
 FLAGS = [
