@@ -213,9 +213,12 @@ cp_status_t cp_attn_step_bwd(const void* q, const void* k, const void* v, const 
                              float softmax_scale, int mode, hipStream_t stream);
 
 /* Workspace bytes cp_ring_attn_fwd needs: two staging slots, each for the K
- * and V blocks [B,H,Skv,D] bf16 of up to four ring steps (sixteen blocks),
- * plus the fp32 running output [B,H,Sq,D], each rounded up to 256 bytes.
- * Returns 0 for non-positive sizes. */
+ * and V blocks [B,H,Skv,D] bf16 of up to four ring steps (sixteen blocks);
+ * the fp32 running output [B,H,Sq,D]; and, for launches whose grid is small
+ * enough that each row block's keys are split over two workgroups, the two
+ * halves' fp32 partial outputs and LSE for R = min(65536, B*H*Sq) rows plus
+ * 512 counters; each part rounded up to 256 bytes.  Returns 0 for
+ * non-positive sizes. */
 size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq);
 
 /*

@@ -30,6 +30,8 @@
 #include "cp_ring_plan.h"
 
 using cpattn::StepArgs;
+using cpattn::kSplitMaxBlocks;
+using cpattn::kSplitRows;
 
 static_assert(cpplan::kMerge == cpattn::kFlagMerge && cpplan::kFinalize == cpattn::kFlagFinalize &&
                   cpplan::kWriteO == cpattn::kFlagWriteO,
@@ -577,11 +579,16 @@ size_t cp_ring_attn_workspace_bytes(int B, int H, int Skv, int D, int Sq) {
 
 namespace cpattn {
 
+// Rows of the key-split partial buffers of a ring workspace.
+size_t split_rows(int B, int H, int Sq) { return std::min((size_t)kSplitRows, (size_t)B * H * Sq); }
+
 size_t ring_fwd_workspace_bytes(int B, int H, int Skv, int D, int Sq, int steps_per_launch) {
   if (B <= 0 || H <= 0 || Skv <= 0 || D <= 0 || Sq <= 0 || steps_per_launch <= 0) return 0;
   const size_t kv = round256((size_t)B * H * Skv * D * 2);
   const size_t o = round256((size_t)B * H * Sq * D * 4);
-  return 4 * (size_t)steps_per_launch * kv + o;
+  const size_t R = split_rows(B, H, Sq);
+  const size_t split = round256(2 * R * D * 4) + round256(2 * R * 4) + round256((size_t)kSplitMaxBlocks * 4);
+  return 4 * (size_t)steps_per_launch * kv + o + split;
 }
 
 cp_status_t ring_fwd(const void* q, const cp_chunks_t* q_chunks, const void* const* k_steps,
@@ -632,14 +639,29 @@ cp_status_t ring_fwd(const void* q, const cp_chunks_t* q_chunks, const void* con
         return fail(CP_ERR_INVALID, "out, lse and workspace must not overlap");
   }
 
+  // workspace: staging slots, running O, key-split partials (O, LSE) and counters
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float* o_run = reinterpret_cast<float*>(ws + 4 * (size_t)steps_per_launch * round256(kv_bytes));
+  unsigned char* p = ws + 4 * (size_t)steps_per_launch * round256(kv_bytes);
+  float* o_run = reinterpret_cast<float*>(p);
+  p += round256(BH * Sq * D * 4);
+  const size_t R = split_rows(B, H, Sq);
+  float* part_o = reinterpret_cast<float*>(p);
+  p += round256(2 * R * D * 4);
+  float* part_lse = reinterpret_cast<float*>(p);
+  p += round256(2 * R * 4);
+  unsigned* part_cnt = reinterpret_cast<unsigned*>(p);
+  hipError_t e0 = cpattn::launch_zero_u32(part_cnt, kSplitMaxBlocks, stream);
+  if (e0 != hipSuccess) return hip_fail(e0, "counter fill launch");
   st = ring_replay(q_chunks, k_steps, v_steps, kv_chunks_steps, n_steps, steps_per_launch, kv_bytes, ws, stream,
                    copy_stream,
                    [&](const RingLaunch& rl) -> hipError_t {
                        StepArgs a;
                        base_args(a, q, rl.k[0], rl.v[0], o_run, lse, out, B, H, D, q_chunks,
                                  &kv_chunks_steps[rl.first_step], softmax_scale);
+                       a.part_o = part_o;
+                       a.part_lse = part_lse;
+                       a.part_cnt = part_cnt;
+                       a.part_rows = (int)R;
                        for (int i = 1; i < rl.count; ++i)
                          add_kv_block(a, rl.k[i], rl.v[i], &kv_chunks_steps[rl.first_step + i]);
                        for (int c : rl.active) a.flags[c] = rl.flags[c] | cpattn::kFlagLaneO;

@@ -41,7 +41,22 @@ struct StepArgs {
   int rb_per_chunk;           // row blocks per query chunk
   int heads_per_xcd;          // > 0: keep each (b,h) on one XCD
   float scale_log2;           // tau * log2(e)
+  // Key split (launch_step may split each row block's key tiles over two
+  // workgroups when the grid is small and these are set): the two halves'
+  // normalised partials, fp32 [2][part_rows][D] in the lane order of the
+  // running O, their LSE [2][part_rows], and one counter per row block, zero
+  // before the launch (the merging workgroup resets it).
+  float* part_o;
+  float* part_lse;
+  unsigned* part_cnt;
+  int part_rows;              // capacity in rows; 0: no key split
 };
+
+// Rows of the key-split partial buffers a ring workspace holds: a launch
+// splits only when its grid of 128-row workgroups has fewer than
+// kSplitMaxBlocks workgroups, so it never needs more rows than this.
+constexpr int kSplitMaxBlocks = 512;
+constexpr int kSplitRows = kSplitMaxBlocks * 128;
 
 // Everything one backward launch of one K/V block needs (both backward
 // kernels); passed by value.
@@ -89,6 +104,9 @@ hipError_t launch_step(const StepArgs& a, int D, hipStream_t stream, const char*
 // staging slot on `stream` (the copy stream of the ring driver).
 hipError_t launch_stage_copy(const void* k_src, void* k_dst, const void* v_src, void* v_dst, size_t bytes,
                              hipStream_t stream);
+
+// Zero n 32-bit words (the key-split counters) with a fill kernel.
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream);
 
 // A single-wave spin of `us` microseconds of the device's constant-rate
 // clock on `stream` (stream-ordering tests only); it always ends.

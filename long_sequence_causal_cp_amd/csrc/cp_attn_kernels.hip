@@ -43,6 +43,15 @@ namespace {
 // sub-tile.
 constexpr float kSumLimit = 256.0f;
 
+// Buffer-resource word 3 of a raw byte buffer, and the cache-policy argument
+// of the buffer load/store builtins that makes an access device-coherent
+// (scope bit SC1).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kDeviceCoherent = 16;
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // max / sum with the partner lane (lane ^ 32): v_permlane32_swap returns each
 // lane's own value and its partner's, in some order.
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -58,13 +67,10 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // 64-key LDS tile): sub-iteration u computes the exponentials of sub-tile u
 // while its MFMAs are QK^T of sub-tile u+1 and PV of sub-tile u-1, neither of
 // which depends on that sub-iteration's VALU work, so the two streams
-// interleave freely.  A wave owns NG groups of 32 query rows; every K and V
-// operand it reads from LDS feeds one MFMA per group, so NG = 2 halves the
-// LDS reads per MFMA (at twice the registers per wave).
-template <int D, int NW, int NG>
+// interleave freely.
+template <int D, int NW, bool kSplit>
 __device__ __forceinline__ void step_body(const StepArgs& a) {
-  constexpr int RW = 32 * NG;  // query rows per wave
-  constexpr int BM = RW * NW;
+  constexpr int BM = 32 * NW;
   constexpr int NS = D / 16;   // k-steps of the QK^T MFMA
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
   constexpr int TB = kTileKeys * D * 2;
@@ -83,7 +89,19 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   const int lq = lane & 31;
 
   // ---- which (row block, batch*head) this workgroup owns ----
-  const int job = blockIdx.x;
+  // With a key split (kSplit) two workgroups share a row block, each over
+  // half of its key tiles; `ks` says which half.  The pair keeps the same
+  // job number modulo 8, so both halves run on one XCD.
+  int job = blockIdx.x, ks = 0;
+  if constexpr (kSplit) {
+    if (a.heads_per_xcd > 0) {
+      ks = (job >> 3) & 1;
+      job = (job & 7) | ((job >> 4) << 3);
+    } else {
+      ks = job & 1;
+      job >>= 1;
+    }
+  }
   int rb_idx, bh;
   if (a.heads_per_xcd > 0) {
     // workgroups are dealt to the 8 XCDs round-robin: keep each head's row
@@ -102,8 +120,8 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   const int q_local0 = qc * a.q_chunk_len + rbi * BM;
   const int q_pos0 = a.q_start[qc] + rbi * BM;
   const int q_posmax = q_pos0 + BM - 1;
-  const int qw_local = q_local0 + wave * RW;
-  const int qw_pos = q_pos0 + wave_u * RW;  // group j's rows start at qw_pos + 32 j
+  const int qw_local = q_local0 + wave * 32;
+  const int qw_pos = q_pos0 + wave_u * 32;
   const size_t bh_q = (size_t)bh * a.Sq;
   const size_t bh_kv = (size_t)bh * a.Skv;
 
@@ -154,25 +172,19 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   auto load_k = [&](const Cursor& t, unsigned char* buf) { k_loader(t.kp, buf, wave_u); };
   auto load_v = [&](const Cursor& t, unsigned char* buf) { v_loader(t.vp, buf, wave_u); };
 
-  // Q^T fragments: in group j, lane holds Q[row 32 j + lq][16s + 8g .. +8]
-  bf16x8 qf[NG][NS];
+  // Q^T fragments: lane holds Q[row lq][16s + 8g .. +8]
+  bf16x8 qf[NS];
+  {
+    const uint16_t* qrow = a.q + (bh_q + qw_local + lq) * D + 8 * g;
 #pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    const uint16_t* qrow = a.q + (bh_q + qw_local + 32 * j + lq) * D + 8 * g;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qf[j][s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+    for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
   }
 
-  f32x16 oacc[NG][NDB];
-  float m_run[NG];   // running max, log2-scaled units
-  float l_lane[NG];  // this lane's share of the row sum
+  f32x16 oacc[NDB];
 #pragma unroll
-  for (int j = 0; j < NG; ++j) {
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) oacc[j][i] = f32x16{};
-    m_run[j] = neg_inf();
-    l_lane[j] = 0.f;
-  }
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+  float m_run = neg_inf();  // running max, log2-scaled units
+  float l_lane = 0.f;       // this lane's share of the row sum
 
   // per-lane constant parts of the LDS reads
   const int k_base = k_lds_off(lq, 0, g);
@@ -186,24 +198,20 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   for (int db = 0; db < NDB; ++db)
     tr_off[db] = tr_row * (D * 2) + (((4 * db + 2 * (G & 1) + ((j16 & 3) >> 1)) ^ tr_swz) << 4) + tr_colbyte;
 
-  using Scores = f32x16[NG];
-  using Probs = bf16x8[NG][2];
-
-  // S^T of one 32-key sub-tile for every group: K rows [32h, 32h+32) of the tile in `kb`
-  auto qk_sub = [&](const unsigned char* kb, int h, Scores& s) {
-#pragma unroll
-    for (int j = 0; j < NG; ++j) s[j] = f32x16{};
+  // S^T of one 32-key sub-tile: K rows [32h, 32h+32) of the tile in `kb`
+  auto qk_sub = [&](const unsigned char* kb, int h) {
+    f32x16 s = {};
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + k_base + st * 2048 + h * 1024);
-#pragma unroll
-      for (int j = 0; j < NG; ++j) s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][st], s[j], 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s, 0, 0, 0);
     }
+    return s;
   };
 
-  // Exponentials of one group's sub-tile against the shift `negm` (minus the
-  // row's reference maximum): P(u) in bf16 and this lane's share of its row
-  // sum, summed in fp32 before rounding.
+  // Exponentials of one sub-tile against the shift `negm` (minus the row's
+  // reference maximum): P(u) in bf16 and this lane's share of its row sum,
+  // summed in fp32 before rounding.
   auto exps = [&](const f32x16& s_cur, bf16x8 (&p_cur)[2], float negm) {
     float lsum = 0.f;
 #pragma unroll
@@ -217,34 +225,29 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     return lsum;
   };
 
-  // The branch-free body of sub-iteration u, for every group.
+  // The branch-free body of sub-iteration u.
   //   exp:  16 exponentials per lane of s_cur (scores of sub-tile u) against
   //         the running maximum as it stands, packed to bf16 into p_cur, and
   //         their row sum (returned in lsum);
   //   QK:   s_nxt = K Q^T of sub-tile u+1, rows [32 hn, +32) of `kn` (kQK);
   //   PV:   O^T += V^T P^T of sub-tile u-1, rows [32 hp, +32) of `vp` (kPV).
-  // Returns a mask with bit j set in a lane whose group-j exponentials must be
-  // redone with a new maximum: its sum exceeds kSumLimit (inf or NaN while the
-  // row has no maximum yet, m_run = -inf).
-  auto body = [&](const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev, const unsigned char* kn,
-                  int hn, const unsigned char* vp, int hp, float (&lsum)[NG], auto exp_tag, auto qk_tag,
-                  auto pv_tag) {
+  // Returns true in a lane whose exponentials must be redone with a new
+  // maximum: its sum exceeds kSumLimit (inf or NaN while the row has no
+  // maximum yet, m_run = -inf).
+  auto body = [&](const f32x16& s_cur, f32x16& s_nxt, bf16x8 (&p_cur)[2], const bf16x8 (&p_prev)[2],
+                  const unsigned char* kn, int hn, const unsigned char* vp, int hp, float& lsum, auto exp_tag,
+                  auto qk_tag, auto pv_tag) {
     constexpr bool kExp = decltype(exp_tag)::value;
     constexpr bool kQK = decltype(qk_tag)::value;
     constexpr bool kPV = decltype(pv_tag)::value;
     // MFMA stream: QK^T and PV alternate so that consecutive MFMAs never
     // share an accumulator
-    if constexpr (kQK) {
-#pragma unroll
-      for (int j = 0; j < NG; ++j) s_nxt[j] = f32x16{};
-    }
+    if constexpr (kQK) s_nxt = f32x16{};
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if constexpr (kQK) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kn + k_base + i * 2048 + hn * 1024);
-#pragma unroll
-        for (int j = 0; j < NG; ++j)
-          s_nxt[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][i], s_nxt[j], 0, 0, 0);
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i], s_nxt, 0, 0, 0);
       }
       if constexpr (kPV) {
         if (i < 2 * NDB) {
@@ -253,88 +256,84 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, base));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, base + 8 * (D * 2)));
           const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int j = 0; j < NG; ++j)
-            oacc[j][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, p_prev[j][t], oacc[j][db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, p_prev[t], oacc[db], 0, 0, 0);
         }
       }
     }
-    if constexpr (!kExp) return 0;
+    if constexpr (!kExp) return false;
     // VALU stream.  -m_run is +inf while the row has no maximum: every p is
     // then inf (or NaN where masked) and the test below fails.
-    int redo = 0;
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      lsum[j] = exps(s_cur[j], p_cur[j], -m_run[j]);
-      // use the packed P here: otherwise the compiler sinks the conversions
-      // past the slow-path branch, out of the MFMA stream
-      asm volatile("" ::"v"(p_cur[j][0]), "v"(p_cur[j][1]));
-      redo |= (lsum[j] <= kSumLimit) ? 0 : (1 << j);
-    }
+    lsum = exps(s_cur, p_cur, -m_run);
+    // use the packed P here: otherwise the compiler sinks the conversions
+    // past the slow-path branch, out of the MFMA stream
+    asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]));
     // interleave: each MFMA followed by its share of LDS reads and three
-    // VALU instructions; the remaining VALU work follows the last MFMA.
-    // Three per MFMA measured about 3% faster than four, and faster than two
-    // or than alternating three and four (one group per wave).
-    constexpr int kMfma = NG * ((kQK ? NS : 0) + (kPV ? 2 * NDB : 0));
-    constexpr int kDs = NG == 1 ? 2 : 1;
-    __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);
+    // VALU instructions; the remaining VALU work (about a fifth) follows the
+    // last MFMA.  Three per MFMA measured about 3% faster than four, and
+    // faster than two or than alternating three and four.
+    constexpr int kMfma = (kQK ? NS : 0) + (kPV ? 2 * NDB : 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int i = 0; i < kMfma; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
-    return redo;
+    return !(lsum <= kSumLimit);
   };
 
-  auto mask = [&](f32x16& s, int kpos, int qpos) {
+  auto mask = [&](f32x16& s, int kpos) {
+    const int qpos = qw_pos + lq;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kp = kpos + 8 * (r >> 2) + 4 * g + (r & 3);
       if (kp > qpos) s[r] = neg_inf();
     }
   };
-  // Sub-iteration u: mask S(u) (first key at kpos) where it crosses a group's
+  // Sub-iteration u: mask S(u) (first key at kpos) if it crosses this wave's
   // diagonal and run the body.  Rarely (on a row's first sub-tile, and when
   // the scores outgrow the running maximum) the slow path raises every row
-  // maximum of the group to its sub-tile maximum, rescales the output (PV(u-1)
+  // maximum of the wave to its sub-tile maximum, rescales the output (PV(u-1)
   // is in by then) and redoes the exponentials.
-  auto sub = [&](int kpos, Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev, const unsigned char* kn,
-                 int hn, const unsigned char* vp, int hp, auto exp_tag, auto qk_tag, auto pv_tag) {
+  auto sub = [&](int kpos, f32x16& s_cur, f32x16& s_nxt, bf16x8 (&p_cur)[2], const bf16x8 (&p_prev)[2],
+                 const unsigned char* kn, int hn, const unsigned char* vp, int hp, auto exp_tag, auto qk_tag,
+                 auto pv_tag) {
     constexpr bool kExp = decltype(exp_tag)::value;
     if constexpr (kExp) {
-#pragma unroll
-      for (int j = 0; j < NG; ++j)
-        if (kpos + 31 > qw_pos + 32 * j) mask(s_cur[j], kpos, qw_pos + 32 * j + lq);
+      if (kpos + 31 > qw_pos) mask(s_cur, kpos);
     }
-    float lsum[NG];
-    const int redo = body(s_cur, s_nxt, p_cur, p_prev, kn, hn, vp, hp, lsum, exp_tag, qk_tag, pv_tag);
+    float lsum = 0.f;
+    const bool redo = body(s_cur, s_nxt, p_cur, p_prev, kn, hn, vp, hp, lsum, exp_tag, qk_tag, pv_tag);
     if constexpr (kExp) {
+      float alpha = 1.f;
+      if (__any(redo)) {
+        float mx = neg_inf();
 #pragma unroll
-      for (int j = 0; j < NG; ++j) {
-        float alpha = 1.f;
-        if (__any((redo >> j) & 1)) {
-          float mx = neg_inf();
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+        mx = xhalf_max(mx) * a.scale_log2;
+        const float m_new = fmaxf(m_run, mx);
+        alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        lsum = exps(s_cur, p_cur, (m_run == neg_inf()) ? 0.f : -m_run);
+        if (__any(alpha != 1.f)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[j][r]);
-          mx = xhalf_max(mx) * a.scale_log2;
-          const float m_new = fmaxf(m_run[j], mx);
-          alpha = (m_new == m_run[j]) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
-          m_run[j] = m_new;
-          lsum[j] = exps(s_cur[j], p_cur[j], (m_run[j] == neg_inf()) ? 0.f : -m_run[j]);
-          if (__any(alpha != 1.f)) {
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[j][db][r] *= alpha;
-          }
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
-        l_lane[j] = __builtin_fmaf(l_lane[j], alpha, lsum[j]);
       }
+      l_lane = __builtin_fmaf(l_lane, alpha, lsum);
     }
   };
   // Cursors at pair n: tm = tile n, tv = tile n+1, tk = tile n+2.
   Cursor tm = chunk_after(-1);
+  if constexpr (kSplit) {
+    // the first half of the visible tiles, or the rest
+    const int half = (T + 1) >> 1;
+    if (ks == 1)
+      for (int i = 0; i < half; ++i) tm = next_tile(tm);
+    T = ks == 0 ? half : T - half;
+  }
   Cursor tv = next_tile(tm);
   Cursor tk = next_tile(tv);
   // Top of tile pair n: K(n+1) and V(n) have landed and every wave is done
@@ -363,9 +362,9 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     load_v(tm, lds_v0);
     wait_vmem_all();
     __syncthreads();
-    Scores sa, sb;
-    Probs pa, pb;
-    qk_sub(lds_k0, 0, sa);
+    f32x16 sa, sb;
+    bf16x8 pa[2], pb[2];
+    sa = qk_sub(lds_k0, 0);
     sub(tm.kpos, sa, sb, pa, pb, lds_k0, 1, lds_v0, 0, Yes{}, Yes{}, No{});
     int n = 0;
     // full pairs n = 0 .. T-2, two per trip (even n, then odd n)
@@ -396,71 +395,154 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
     }
   }
 
-  // ---- epilogue: normalise, LSE, merge, write (per group of 32 rows) ----
-  const bool write_o = (flags & kFlagWriteO) != 0;
-  const bool finalize = (flags & kFlagFinalize) != 0;
-  const bool lane_order = (flags & kFlagLaneO) != 0;
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    const float l = xhalf_sum(l_lane[j]);
-    const float lse_j = (l > 0.f) ? (m_run[j] + __log2f(l)) * kLn2 : neg_inf();
-    const float inv_l = (l > 0.f) ? 1.f / l : 0.f;
-    const size_t row0 = bh_q + qw_local + 32 * j;  // the group's first row
-    const size_t row = row0 + lq;
-    float w_prev = 0.f, w_cur = inv_l, lse_new = lse_j;
-    if (flags & kFlagMerge) {
-      const float lp = a.lse_run[row];
-      if (lp != neg_inf()) {
-        if (lse_j == neg_inf()) {
-          w_prev = 1.f;
-          w_cur = 0.f;
-          lse_new = lp;
-        } else {
-          const float x2 = lp * kLog2e, y2 = lse_j * kLog2e;
-          const float mm = fmaxf(x2, y2);
-          const float L2 = mm + __log2f(exp2f(x2 - mm) + exp2f(y2 - mm));
-          w_prev = exp2f(x2 - L2);
-          w_cur = exp2f(y2 - L2) * inv_l;
-          lse_new = L2 * kLn2;
-        }
-      }
-    }
-    if (g == 0) a.lse_run[row] = lse_new;
-    // The running O of a group's 32 rows occupies the 32 x D floats at
-    // o_run + row0 D.  In row-major order a lane's 16-byte piece (d0 .. d0+3
-    // of row lq) lands 32 rows apart from its neighbours' pieces; in lane
-    // order (kFlagLaneO, the ring driver's private workspace) piece k of lane
-    // L is the 16 bytes at float (64 k + L) 4 of the block, so each wave load
-    // or store covers one contiguous KiB.  Either way piece k = 4 db + rr
-    // sits at o_base + k * o_stride.
-    float* const o_base = a.o_run + row0 * D + (lane_order ? lane * 4 : lq * D + 4 * g);
-    const int o_stride = lane_order ? 256 : 8;
+  // ---- epilogue: normalise, LSE, merge, write ----
+  const float l = xhalf_sum(l_lane);
+  const float lse_j = (l > 0.f) ? (m_run + __log2f(l)) * kLn2 : neg_inf();
+  const float inv_l = (l > 0.f) ? 1.f / l : 0.f;
+  const size_t row = bh_q + qw_local + lq;
+  // This launch's partial for the row: oacc * inv_l with log-sum-exp lse_c,
+  // or, with a key split, the two halves' normalised partials p0, p1 merged
+  // as w0 * p0 + w1 * p1.
+  float lse_c = lse_j, w0 = 0.f, w1 = 0.f;
+  // key split: the halves' partial outputs and LSE, and the other half's offset
+  const size_t slot_rows = (size_t)a.part_rows;
+  const __amdgpu_buffer_rsrc_t po =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_o, 0, (int)(2 * slot_rows * D * sizeof(float)), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t pl =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_lse, 0, (int)(2 * slot_rows * sizeof(float)), kBufferRsrcWord3);
+  int oth_off = 0;
+  if constexpr (kSplit) {
+    // Both halves write their normalised partial (lane order) and LSE to
+    // their own slot and count in on the row block's counter; the second to
+    // arrive merges the two and goes on, the first is done.  Nothing waits
+    // on the other half.  The partials go through device-coherent accesses
+    // (write-through stores, loads that do not hit a stale cached copy), so
+    // no cache-wide write-back or invalidate is needed: the stores have
+    // completed before the count, and the count is a device-scope atomic.
+    // The merge uses the partials in the halves' order (the arriving half's
+    // own values equal what it stored), so the result does not depend on
+    // which half arrives last.
+    const size_t prow0 = (size_t)job * BM + 32 * wave;  // the wave's first slot row
+    const int my_o = (int)((((size_t)ks * slot_rows + prow0) * D + lane * 4) * sizeof(float));
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = 32 * db + 8 * rr + 4 * g;
-        float* const o_ptr = o_base + (4 * db + rr) * o_stride;
         f32x4 o;
-        o[0] = oacc[j][db][4 * rr + 0] * w_cur;
-        o[1] = oacc[j][db][4 * rr + 1] * w_cur;
-        o[2] = oacc[j][db][4 * rr + 2] * w_cur;
-        o[3] = oacc[j][db][4 * rr + 3] * w_cur;
-        if (w_prev != 0.f) {
-          const f32x4 prev = *reinterpret_cast<const f32x4*>(o_ptr);
-          o += w_prev * prev;
-        }
-        if (write_o) *reinterpret_cast<f32x4*>(o_ptr) = o;
-        if (finalize) {
-          bf16x4 h;
-          h[0] = (__bf16)o[0];
-          h[1] = (__bf16)o[1];
-          h[2] = (__bf16)o[2];
-          h[3] = (__bf16)o[3];
-          *reinterpret_cast<bf16x4*>(a.out + row * D + d0) = h;
-        }
+        o[0] = oacc[db][4 * rr + 0] * inv_l;
+        o[1] = oacc[db][4 * rr + 1] * inv_l;
+        o[2] = oacc[db][4 * rr + 2] * inv_l;
+        o[3] = oacc[db][4 * rr + 3] * inv_l;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), po, my_o + (4 * db + rr) * 256 * 4, 0,
+                                               kDeviceCoherent);
       }
+    if (g == 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_j), pl,
+                                            (int)(((size_t)ks * slot_rows + prow0 + lq) * sizeof(float)), 0,
+                                            kDeviceCoherent);
+    // Wait until this wave's stores have completed (a device-scope release
+    // fence would also write back and invalidate the whole L2, which the
+    // write-through stores do not need): s_waitcnt vmcnt(0).
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    __shared__ unsigned arrived;
+    if (threadIdx.x == 0)
+      arrived = __hip_atomic_fetch_add(&a.part_cnt[job], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived == 0) return;  // the other half merges
+    if (threadIdx.x == 0)  // ready for the next launch
+      __hip_atomic_store(&a.part_cnt[job], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int ot = ks ^ 1;
+    const int ot_o = (int)((((size_t)ot * slot_rows + prow0) * D + lane * 4) * sizeof(float));
+    const float l_other = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        pl, (int)(((size_t)ot * slot_rows + prow0 + lq) * sizeof(float)), 0, kDeviceCoherent));
+    oth_off = ot_o;
+    const float l0 = ks == 0 ? lse_j : l_other, l1 = ks == 0 ? l_other : lse_j;
+    if (l0 == neg_inf()) {
+      w1 = (l1 == neg_inf()) ? 0.f : 1.f;
+      lse_c = l1;
+    } else if (l1 == neg_inf()) {
+      w0 = 1.f;
+      lse_c = l0;
+    } else {
+      const float x2 = l0 * kLog2e, y2 = l1 * kLog2e;
+      const float mm = fmaxf(x2, y2);
+      const float L2 = mm + __log2f(exp2f(x2 - mm) + exp2f(y2 - mm));
+      w0 = exp2f(x2 - L2);
+      w1 = exp2f(y2 - L2);
+      lse_c = L2 * kLn2;
+    }
   }
+  // merge with the running result of earlier launches
+  float w_prev = 0.f, w_cur = 1.f, lse_new = lse_c;
+  if (flags & kFlagMerge) {
+    const float lp = a.lse_run[row];
+    if (lp != neg_inf()) {
+      if (lse_c == neg_inf()) {
+        w_prev = 1.f;
+        w_cur = 0.f;
+        lse_new = lp;
+      } else {
+        const float x2 = lp * kLog2e, y2 = lse_c * kLog2e;
+        const float mm = fmaxf(x2, y2);
+        const float L2 = mm + __log2f(exp2f(x2 - mm) + exp2f(y2 - mm));
+        w_prev = exp2f(x2 - L2);
+        w_cur = exp2f(y2 - L2);
+        lse_new = L2 * kLn2;
+      }
+    }
+  }
+  const float w_self = w_cur * inv_l;
+  if (g == 0) a.lse_run[row] = lse_new;
+  const bool write_o = (flags & kFlagWriteO) != 0;
+  const bool finalize = (flags & kFlagFinalize) != 0;
+  // The running O of this wave's 32 rows occupies the 32 x D floats at
+  // o_run + (bh_q + qw_local) D.  In row-major order a lane's 16-byte piece
+  // (d0 .. d0+3 of row lq) lands 32 rows apart from its neighbours' pieces;
+  // in lane order (kFlagLaneO, the ring driver's private workspace) piece k
+  // of lane L is the 16 bytes at float (64 k + L) 4 of the block, so each
+  // wave load or store covers one contiguous KiB.
+  // Either way piece k = 4 db + rr sits at o_base + k * o_stride.
+  const bool lane_order = (flags & kFlagLaneO) != 0;
+  float* const o_base = a.o_run + (bh_q + qw_local) * D + (lane_order ? lane * 4 : lq * D + 4 * g);
+  const int o_stride = lane_order ? 256 : 8;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int d0 = 32 * db + 8 * rr + 4 * g;
+      float* const o_ptr = o_base + (4 * db + rr) * o_stride;
+      f32x4 o;
+      if constexpr (kSplit) {
+        f32x4 own, oth = __builtin_bit_cast(
+                       f32x4, __builtin_amdgcn_raw_buffer_load_b128(po, oth_off + (4 * db + rr) * 256 * 4, 0,
+                                                                    kDeviceCoherent));
+        own[0] = oacc[db][4 * rr + 0] * inv_l;
+        own[1] = oacc[db][4 * rr + 1] * inv_l;
+        own[2] = oacc[db][4 * rr + 2] * inv_l;
+        own[3] = oacc[db][4 * rr + 3] * inv_l;
+        const f32x4 p0 = ks == 0 ? own : oth, p1 = ks == 0 ? oth : own;
+        o = (p0 * w0 + p1 * w1) * w_cur;
+      } else {
+        o[0] = oacc[db][4 * rr + 0] * w_self;
+        o[1] = oacc[db][4 * rr + 1] * w_self;
+        o[2] = oacc[db][4 * rr + 2] * w_self;
+        o[3] = oacc[db][4 * rr + 3] * w_self;
+      }
+      if (w_prev != 0.f) {
+        const f32x4 prev = *reinterpret_cast<const f32x4*>(o_ptr);
+        o += w_prev * prev;
+      }
+      if (write_o) *reinterpret_cast<f32x4*>(o_ptr) = o;
+      if (finalize) {
+        bf16x4 h;
+        h[0] = (__bf16)o[0];
+        h[1] = (__bf16)o[1];
+        h[2] = (__bf16)o[2];
+        h[3] = (__bf16)o[3];
+        *reinterpret_cast<bf16x4*>(a.out + row * D + d0) = h;
+      }
+    }
 }
 
 // Entry points.  Eight-wave workgroups (256 rows) run two waves per SIMD and
@@ -469,25 +551,32 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
 // (chunk lengths that are not multiples of 256) run one wave per SIMD.
 template <int D>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_num_vgpr(124))) step_kernel_256(const StepArgs a) {
-  step_body<D, 8, 1>(a);
+  step_body<D, 8, false>(a);
 }
-// 256-row workgroups of four waves with 64 rows each, one wave per SIMD:
-// every LDS operand read feeds two MFMAs.  Held to 504 registers so that a
-// staging copy's wave still fits beside it.
+// The same with each row block's key tiles split over two workgroups: for
+// grids of 256-row blocks that would leave compute units idle and hold no
+// diagonal chunk pair.  The halves' partials meet in the workspace and the
+// second to finish merges them.
 template <int D>
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(252))) step_kernel_256x2(const StepArgs a) {
-  step_body<D, 4, 2>(a);
+__global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_num_vgpr(124))) step_kernel_256s(const StepArgs a) {
+  step_body<D, 8, true>(a);
 }
 // 128-row workgroups held to the same register budget, two per CU: for grids
 // of 256-row workgroups that would leave compute units idle, and for chunk
 // lengths that are multiples of 128 but not of 256.
 template <int D>
 __global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_num_vgpr(124))) step_kernel_128(const StepArgs a) {
-  step_body<D, 4, 1>(a);
+  step_body<D, 4, false>(a);
+}
+// The same with the key split (grids with a diagonal chunk pair whose
+// 128-row workgroups would hold at most one wave per SIMD).
+template <int D>
+__global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_num_vgpr(124))) step_kernel_128s(const StepArgs a) {
+  step_body<D, 4, true>(a);
 }
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) step_kernel_small(const StepArgs a) {
-  step_body<D, NW, 1>(a);
+  step_body<D, NW, false>(a);
 }
 
 // ---- standalone log-sum-exp merge, HBM-bound elementwise pass ----
@@ -583,6 +672,17 @@ __global__ void __launch_bounds__(64) delay_kernel(long long ticks) {
 
 }  // namespace
 
+__global__ void __launch_bounds__(256) zero_u32_kernel(unsigned* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_delay(int us, hipStream_t stream) {
   if (us <= 0) return hipSuccess;
   hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, stream, 100LL * us);
@@ -619,20 +719,38 @@ hipError_t launch_step(const StepArgs& args, int D, hipStream_t stream, const ch
   bool diag = false;
   for (int i = 0; i < a.n_order; ++i)
     for (int k = 0; k < a.n_kv_chunks; ++k) diag = diag || a.q_start[a.order[i]] == a.kv_start[k];
+  // Key split (needs the caller's partial buffers: the ring driver's
+  // workspace): each row block's key tiles are split over two workgroups
+  // whose partials are merged by log-sum-exp.  Taken for a 256-row grid
+  // without a diagonal pair that would leave compute units idle (its halves
+  // then keep the eight-wave blocks), and for a 128-row grid that holds fewer
+  // than two workgroups per compute unit.
   const long long g256 = (long long)a.n_order * (a.q_chunk_len / 256) * a.BH;
-  if (bm == 256 && (g256 < device_cus() || (diag && g256 <= device_cus()))) bm = 128;
+  const auto split_fits = [&](long long grid_rows) {
+    return a.part_rows > 0 && grid_rows <= a.part_rows;
+  };
+  bool split = false;
+  if (bm == 256 && !diag && g256 < device_cus() && g256 <= kSplitMaxBlocks && split_fits(g256 * 256))
+    split = true;
+  else if (bm == 256 && (g256 < device_cus() || (diag && g256 <= device_cus())))
+    bm = 128;
   a.rb_per_chunk = a.q_chunk_len / bm;
   const long long grid = (long long)a.n_order * a.rb_per_chunk * a.BH;
   if (name) *name = nullptr;
   if (grid <= 0) return hipSuccess;
-  const dim3 g((unsigned)grid), blk((unsigned)(2 * bm));  // one wave per 32 rows
+  if (bm == 128 && grid < 2LL * device_cus() && grid <= kSplitMaxBlocks && split_fits(grid * 128)) split = true;
+  const dim3 g((unsigned)(split ? 2 * grid : grid)), blk((unsigned)(2 * bm));  // one wave per 32 rows
   const char* n;
   if (D == 128) {
-    if (bm == 256) { hipLaunchKernelGGL((step_kernel_256<128>), g, blk, 0, stream, a); n = "step_kernel_256<128>"; }
+    if (bm == 256 && split) { hipLaunchKernelGGL((step_kernel_256s<128>), g, blk, 0, stream, a); n = "step_kernel_256s<128>"; }
+    else if (bm == 256) { hipLaunchKernelGGL((step_kernel_256<128>), g, blk, 0, stream, a); n = "step_kernel_256<128>"; }
+    else if (split) { hipLaunchKernelGGL((step_kernel_128s<128>), g, blk, 0, stream, a); n = "step_kernel_128s<128>"; }
     else if (bm == 128) { hipLaunchKernelGGL((step_kernel_128<128>), g, blk, 0, stream, a); n = "step_kernel_128<128>"; }
     else { hipLaunchKernelGGL((step_kernel_small<128, 2>), g, blk, 0, stream, a); n = "step_kernel_small<128, 2>"; }
   } else {
-    if (bm == 256) { hipLaunchKernelGGL((step_kernel_256<64>), g, blk, 0, stream, a); n = "step_kernel_256<64>"; }
+    if (bm == 256 && split) { hipLaunchKernelGGL((step_kernel_256s<64>), g, blk, 0, stream, a); n = "step_kernel_256s<64>"; }
+    else if (bm == 256) { hipLaunchKernelGGL((step_kernel_256<64>), g, blk, 0, stream, a); n = "step_kernel_256<64>"; }
+    else if (split) { hipLaunchKernelGGL((step_kernel_128s<64>), g, blk, 0, stream, a); n = "step_kernel_128s<64>"; }
     else if (bm == 128) { hipLaunchKernelGGL((step_kernel_128<64>), g, blk, 0, stream, a); n = "step_kernel_128<64>"; }
     else { hipLaunchKernelGGL((step_kernel_small<64, 2>), g, blk, 0, stream, a); n = "step_kernel_small<64, 2>"; }
   }

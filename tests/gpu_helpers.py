@@ -103,12 +103,23 @@ def oracle_rows(Q, K, V, pos_per_head, scale):
     return out, lse
 
 
-def compare(out_gpu, lse_gpu, out_ref, lse_ref, local_rows=None):
-    """Max-abs errors of GPU results (optionally at local_rows [B,H,n]) against the oracle's."""
+# Half an ulp of bf16 is at most 2^-8 of the value: the bf16 output's own rounding.
+BF16_HALF_ULP_REL = 2.0 ** -8
+
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, local_rows=None, output_rounding=False):
+    """Max-abs errors of GPU results (optionally at local_rows [B,H,n]) against the oracle's.
+
+    With output_rounding, the output error is counted beyond the bf16 output's own rounding,
+    max(|out - ref| - 2^-8 |ref|): for stress inputs whose outputs reach magnitudes where half an ulp
+    of bf16 alone approaches the bound (|out| >= 2: 2^-7 and more)."""
     o = out_gpu.float().cpu().numpy()
     l = lse_gpu.cpu().numpy()
     if local_rows is not None:
         o = np.take_along_axis(o, local_rows[..., None], axis=2)
         l = np.take_along_axis(l, local_rows, axis=2)
     assert np.isfinite(o).all() and np.isfinite(l).all()
-    return float(np.max(np.abs(o - out_ref))), float(np.max(np.abs(l - lse_ref)))
+    err = np.abs(o - out_ref)
+    if output_rounding:
+        err = err - BF16_HALF_ULP_REL * np.abs(out_ref)
+    return float(np.max(err)), float(np.max(np.abs(l - lse_ref)))

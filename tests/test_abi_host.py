@@ -79,7 +79,11 @@ def test_zigzag_rejects_bad_arguments(lib, args):
 def test_workspace_bytes(lib):
     B, H, Skv, D, Sq = 1, 32, 4096, 128, 4096
     kv = B * H * Skv * D * 2
-    assert cb.cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq) == 16 * kv + B * H * Sq * D * 4
+    # 2 slots x 4 steps x (K, V), the fp32 running O, and the key-split partials (O and LSE of two
+    # halves for at most 512 * 128 rows) with 512 counters
+    R = min(512 * 128, B * H * Sq)
+    split = 2 * R * D * 4 + 2 * R * 4 + 512 * 4
+    assert cb.cp_ring_attn_workspace_bytes(B, H, Skv, D, Sq) == 16 * kv + B * H * Sq * D * 4 + split
     assert cb.cp_ring_attn_workspace_bytes(1, 1, 64, 64, 64) % 256 == 0
     assert cb.cp_ring_attn_workspace_bytes(0, 1, 64, 64, 64) == 0
 
