@@ -119,6 +119,7 @@ void base_args(StepArgs& a, const void* q, const void* k, const void* v, float* 
   add_kv_block(a, k, v, kvc);
   a.rb_per_chunk = qc->chunk_len / cpattn::step_block_rows(qc->chunk_len);
   a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+  a.heads_per_group = a.heads_per_xcd;
   a.scale_log2 = scale * 1.4426950408889634f;
 }
 
@@ -214,6 +215,7 @@ cpattn::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void
   for (int i = 0; i < a.n_kv_chunks; ++i) a.kv_start[i] = (int)kvc->start[i];
   a.accumulate = mode;
   a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+  a.heads_per_group = a.heads_per_xcd;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   return a;
@@ -465,6 +467,7 @@ cp_status_t cp_attn_step_fwd_fp8(const void* q, const void* k, const void* vt, f
     a.kv_start[i] = (int)kv_chunks->start[i];
   }
   a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+  a.heads_per_group = a.heads_per_xcd;
   a.scale_log2 = softmax_scale * q_scale * k_scale * 1.4426950408889634f;
   a.v_scale = v_scale;
   std::vector<int> idx;
@@ -807,7 +810,8 @@ cp_status_t cp_ring_attn_fwd_fp8(const void* q, const cp_chunks_t* q_chunks, con
                          a.kv_start[a.n_kv_chunks] = (int)t.start[c];
                        }
                      }
-                                        a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+                     a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+                     a.heads_per_group = a.heads_per_xcd;
                      a.scale_log2 = softmax_scale * q_scale * k_scale * 1.4426950408889634f;
                      a.v_scale = v_scale;
                      std::vector<int> idx(rl.active);

@@ -37,19 +37,6 @@
 namespace cpattn {
 namespace {
 
-// XCD-aware job split shared by both kernels: workgroups are dealt to the 8
-// XCDs round-robin, so keep each (b, h) on one XCD and its tiles in that
-// XCD's L2.
-__device__ __forceinline__ void job_split(int job, int BH, int heads_per_xcd, int& blk, int& bh) {
-  if (heads_per_xcd > 0) {
-    const int x = job & 7, kk = job >> 3;
-    blk = kk / heads_per_xcd;
-    bh = x * heads_per_xcd + kk % heads_per_xcd;
-  } else {
-    blk = job / BH;
-    bh = job % BH;
-  }
-}
 
 // Per-lane byte offsets of the transposed (ds_read_b64_tr_b16) reads of a
 // V-layout tile: for 32-row block db of D, the A operand X^T[d][row] of one
@@ -119,7 +106,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a) {
   const int lq = lane & 31;
 
   int rb_idx, bh;
-  job_split(blockIdx.x, a.BH, a.heads_per_xcd, rb_idx, bh);
+  xcd_job(blockIdx.x, a.BH, a.heads_per_xcd, a.heads_per_group, a.Sq / BM, rb_idx, bh);
   const int rb = a.Sq / BM - 1 - rb_idx;  // later rows (more keys) first
   const int q_local0 = rb * BM;
   const int qc = q_local0 / a.q_chunk_len;
@@ -268,7 +255,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   const int lq = lane & 31;
 
   int kb_idx, bh;
-  job_split(blockIdx.x, a.BH, a.heads_per_xcd, kb_idx, bh);
+  xcd_job(blockIdx.x, a.BH, a.heads_per_xcd, a.heads_per_group, a.Skv / BN, kb_idx, bh);
   const int k_local0 = kb_idx * BN;  // earlier keys (more queries) first
   const int kc = k_local0 / a.kv_chunk_len;
   const int k_pos0 = a.kv_start[kc] + (k_local0 - kc * a.kv_chunk_len);
@@ -487,9 +474,25 @@ int bwd_device_cus() {
   }();
   return n;
 }
+
+// Whether the block holds a diagonal chunk pair (a query chunk at a key
+// chunk's position).
+bool bwd_diag(const BwdArgs& a) {
+  bool diag = false;
+  for (int i = 0; i < a.n_q_chunks; ++i)
+    for (int k = 0; k < a.n_kv_chunks; ++k) diag = diag || a.q_start[i] == a.kv_start[k];
+  return diag;
+}
+// Heads per group of the XCD-aware job order: a head's blocks run together
+// (one workgroup per CU), twice as many where block work differs (diagonal).
+int bwd_heads_per_group(const BwdArgs& a, long long blocks_per_head) {
+  if (a.heads_per_xcd <= 0) return 0;
+  return heads_per_group(a.heads_per_xcd, blocks_per_head, (long long)(bwd_device_cus() / 8) * (bwd_diag(a) ? 2 : 1));
+}
 }  // namespace
 
-hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream, const char** name) {
+hipError_t launch_bwd_dq(const BwdArgs& args, hipStream_t stream, const char** name) {
+  BwdArgs a = args;
   // The grid covers every query row of the rank, and in a ring step past the
   // first the rows of one chunk see no key (their workgroups end at once).  Where
   // a grid of 256-row workgroups holds at most one per compute unit, 128-row
@@ -501,6 +504,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream, const char** name
   const long long grid = (long long)a.BH * (a.Sq / bm);
   if (name) *name = nullptr;
   if (grid <= 0) return hipSuccess;
+  a.heads_per_group = bwd_heads_per_group(a, a.Sq / bm);
   const dim3 g((unsigned)grid), blk((unsigned)(2 * bm));  // one wave per 32 rows
   const char* n;
   if (a.D == 128) {
@@ -516,7 +520,8 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream, const char** name
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** name) {
+hipError_t launch_bwd_dkdv(const BwdArgs& args, hipStream_t stream, const char** name) {
+  BwdArgs a = args;
   // In a step that holds a diagonal chunk pair, a grid of 256-key workgroups
   // with at most one per compute unit has blocks whose work ranges from a few
   // query tiles to twice the mean, and with fewer blocks than units it also
@@ -524,13 +529,12 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** na
   // beside the heavy ones and spread the work over more units.  A key's dK, dV
   // are the same either way (its wave sums the same query tiles in order).
   int bn = bwd_dkdv_keys(a.kv_chunk_len);
-  bool diag = false;
-  for (int i = 0; i < a.n_q_chunks; ++i)
-    for (int k = 0; k < a.n_kv_chunks; ++k) diag = diag || a.q_start[i] == a.kv_start[k];
+  const bool diag = bwd_diag(a);
   if (bn == 256 && diag && (long long)a.BH * (a.Skv / 256) <= bwd_device_cus()) bn = 128;
   const long long grid = (long long)a.BH * (a.Skv / bn);
   if (name) *name = nullptr;
   if (grid <= 0) return hipSuccess;
+  a.heads_per_group = bwd_heads_per_group(a, a.Skv / bn);
   const dim3 g((unsigned)grid), blk((unsigned)(2 * bn));  // one wave per 32 keys
   const char* n;
   if (a.D == 128) {

@@ -30,6 +30,7 @@ struct Fp8StepArgs {
   int kv_start[kMaxChunks];
   int rb_per_chunk;                // set by launch_step_fp8 from its row-block choice
   int heads_per_xcd;
+  int heads_per_group;             // set by launch_step_fp8
   float scale_log2;                // tau * q_scale * k_scale * log2(e)
   float v_scale;                   // the dequantisation factor of V
 };

@@ -84,14 +84,7 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
 
   const int job = blockIdx.x;
   int rb_idx, bh;
-  if (a.heads_per_xcd > 0) {
-    const int x = job & 7, kk = job >> 3;
-    rb_idx = kk / a.heads_per_xcd;
-    bh = x * a.heads_per_xcd + kk % a.heads_per_xcd;
-  } else {
-    rb_idx = job / a.BH;
-    bh = job % a.BH;
-  }
+  xcd_job(job, a.BH, a.heads_per_xcd, a.heads_per_group, a.n_order * a.rb_per_chunk, rb_idx, bh);
   const int oi = rb_idx / a.rb_per_chunk;
   const int rbi = a.rb_per_chunk - 1 - rb_idx % a.rb_per_chunk;
   const int qc = a.order[oi];
@@ -224,9 +217,9 @@ __device__ __forceinline__ void fp8_step_body(const Fp8StepArgs& a) {
         e1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][4 * i + r], a.scale_log2, negm));
         lsum += e0[r] + e1[r];
       }
-      int x0 = __builtin_amdgcn_cvt_pk_fp8_f32(e0[0], e0[1], 0, false);
+      int x0 = __builtin_amdgcn_cvt_pk_fp8_f32(e0[0], e0[1], __float_as_int(e0[0]), false);
       x0 = __builtin_amdgcn_cvt_pk_fp8_f32(e0[2], e0[3], x0, true);
-      int x1 = __builtin_amdgcn_cvt_pk_fp8_f32(e1[0], e1[1], 0, false);
+      int x1 = __builtin_amdgcn_cvt_pk_fp8_f32(e1[0], e1[1], __float_as_int(e1[0]), false);
       x1 = __builtin_amdgcn_cvt_pk_fp8_f32(e1[2], e1[3], x1, true);
       auto r = __builtin_amdgcn_permlane32_swap((unsigned)x0, (unsigned)x1, false, false);
       p[2 * i] = (int)r[0];
@@ -491,6 +484,10 @@ hipError_t launch_step_fp8(const Fp8StepArgs& args, hipStream_t stream, const ch
   const long long grid = (long long)a.n_order * a.rb_per_chunk * a.BH;
   if (name) *name = nullptr;
   if (grid <= 0) return hipSuccess;
+  // heads per group of the XCD-aware order, as for the bf16 step kernel
+  if (a.heads_per_xcd > 0)
+    a.heads_per_group = heads_per_group(a.heads_per_xcd, (long long)a.n_order * a.rb_per_chunk,
+                                        (long long)(fp8_device_cus() / 8) * (bm == 256 ? 1 : 2) * (diag ? 2 : 1));
   if (bm == 256)
     hipLaunchKernelGGL(fp8_step_kernel, dim3((unsigned)grid), dim3(512), 0, stream, a);
   else

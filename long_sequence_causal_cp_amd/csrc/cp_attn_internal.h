@@ -40,6 +40,7 @@ struct StepArgs {
   int kv_start[kMaxChunks];
   int rb_per_chunk;           // row blocks per query chunk
   int heads_per_xcd;          // > 0: keep each (b,h) on one XCD
+  int heads_per_group;        // divides heads_per_xcd; set by the launch
   float scale_log2;           // tau * log2(e)
   // Key split (launch_step may split each row block's key tiles over two
   // workgroups when the grid is small and these are set): the two halves'
@@ -78,6 +79,7 @@ struct BwdArgs {
   int kv_start[kMaxChunks];
   int accumulate;        // bit 0: dq += contribution (else =); bit 1: dk, dv += (else =)
   int heads_per_xcd;     // > 0: keep each (b,h) on one XCD
+  int heads_per_group;   // divides heads_per_xcd; set by the launch
   float scale;           // tau
   float scale_log2;      // tau * log2(e)
 };
@@ -93,6 +95,16 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** na
 // delta[r] = sum_d dout[r][d] * out[r][d] over `rows` rows of D bf16 values.
 hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, float* delta, int64_t rows, int D,
                             hipStream_t stream);
+
+// Heads per group of the XCD-aware job order: the most heads (a divisor of
+// heads_per_xcd) whose blocks_per_head workgroups each fit in `slots`, the
+// workgroups one XCD runs at once; at least 1.
+inline int heads_per_group(int heads_per_xcd, long long blocks_per_head, long long slots) {
+  int hpg = 1;
+  for (int d = 1; d <= heads_per_xcd; ++d)
+    if (heads_per_xcd % d == 0 && d * blocks_per_head <= slots) hpg = d;
+  return hpg;
+}
 
 // Row-block height (queries per workgroup) the step kernel uses for a chunk length.
 int step_block_rows(int q_chunk_len);

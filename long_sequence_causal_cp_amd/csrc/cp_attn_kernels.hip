@@ -102,17 +102,9 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
       job >>= 1;
     }
   }
+  // the row block's index (heaviest first, see below) and (b, h)
   int rb_idx, bh;
-  if (a.heads_per_xcd > 0) {
-    // workgroups are dealt to the 8 XCDs round-robin: keep each head's row
-    // blocks on one XCD so its K/V tiles are shared through that XCD's L2
-    const int x = job & 7, kk = job >> 3;
-    rb_idx = kk / a.heads_per_xcd;
-    bh = x * a.heads_per_xcd + kk % a.heads_per_xcd;
-  } else {
-    rb_idx = job / a.BH;
-    bh = job % a.BH;
-  }
+  xcd_job(job, a.BH, a.heads_per_xcd, a.heads_per_group, a.n_order * a.rb_per_chunk, rb_idx, bh);
   const int oi = rb_idx / a.rb_per_chunk;
   const int rbi = a.rb_per_chunk - 1 - rb_idx % a.rb_per_chunk;  // later rows (more keys) first
   const int qc = a.order[oi];
@@ -739,6 +731,18 @@ hipError_t launch_step(const StepArgs& args, int D, hipStream_t stream, const ch
   if (name) *name = nullptr;
   if (grid <= 0) return hipSuccess;
   if (bm == 128 && grid < 2LL * device_cus() && grid <= kSplitMaxBlocks && split_fits(grid * 128)) split = true;
+  // Heads per group: the most heads (a divisor of an XCD's share) whose row
+  // blocks fit in what one XCD runs at once (one 256-row or two 128-row
+  // workgroups per CU, two workgroups per row block with the key split), so
+  // that a head's row blocks run together and share its K/V tiles in the
+  // L2.  A launch with a diagonal chunk pair, whose row blocks' work differs,
+  // allows twice that: heaviest-first order then spans two rounds of
+  // workgroups, which keeps the tail short.
+  if (a.heads_per_xcd > 0) {
+    const long long rb_per_head = (long long)a.n_order * a.rb_per_chunk * (split ? 2 : 1);
+    const long long slots = (long long)(device_cus() / 8) * (bm == 256 ? 1 : 2) * (diag ? 2 : 1);
+    a.heads_per_group = heads_per_group(a.heads_per_xcd, rb_per_head, slots);
+  }
   const dim3 g((unsigned)(split ? 2 * grid : grid)), blk((unsigned)(2 * bm));  // one wave per 32 rows
   const char* n;
   if (D == 128) {
