@@ -217,6 +217,45 @@ def test_fp8_ring_batch_heads_xcd_mapping(rank, L):
     assert eo <= tol and el <= LSE_TOL, (eo, tol, el)
 
 
+@pytest.mark.parametrize("rank", [0, 1])
+def test_fp8_ring_head_groups(rank):
+    """Batch 2 x 32 heads, 2048-token chunks: 8 heads per XCD whose row blocks (8 per chunk) exceed what an
+    XCD runs at once, so the launches take the XCD's heads in groups (4 of the 8 in a group launch).
+    Sampled rows of (batch, head) pairs from different groups and XCDs against the oracle."""
+    B, H, D, N, L = 2, 32, 128, 2, 2048
+    S = 2 * N * L
+    Q, K, V = workloads.make_qkv_scaled((B, H, S, D), 640 + rank)
+    (qc, sq), (kc, sk), (vc, sv) = quantize(Q.float()), quantize(K.float()), quantize(V.float())
+    heads = [(0, 0), (0, 13), (1, 7), (1, 30)]
+    deq = {}
+    for name, (c, s) in zip("QKV", ((qc, sq), (kc, sk), (vc, sv))):
+        deq[name] = {bh: dequantize(c[bh[0]:bh[0] + 1, bh[1]:bh[1] + 1], s)[0, 0] for bh in heads}
+    scale = 1.0 / np.sqrt(D)
+    print("[case] fp8 ring head groups B", B, "H", H, "N", N, "L", L, "rank", rank, flush=True)
+    q_tab, kv_tabs = zigzag_tables(N, rank, L)
+    q = _gather(qc, q_tab).to(DEV)
+    ks = [_gather(kc, t).to(DEV) for t in kv_tabs]
+    vts = [_gather(vc, t).view(torch.uint8).transpose(2, 3).contiguous().view(torch.float8_e4m3fn).to(DEV)
+           for t in kv_tabs]
+    Sq = q.shape[2]
+    ws = torch.empty(cp.cp_ring_attn_fwd_fp8_workspace_bytes(B, H, ks[0].shape[2], D, Sq), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty((B, H, Sq, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+    cp.cp_ring_attn_fwd_fp8(q, q_tab, ks, vts, kv_tabs, out, lse, scale, sq, sk, sv, ws,
+                            copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    qpos = positions(q_tab)
+    local = np.unique(np.concatenate([np.random.default_rng(rank).choice(Sq, 96, replace=False),
+                                      [0, L - 1, L, Sq - 1]]))
+    segs = ring_segments(_tables(kv_tabs), grouped=True)
+    for bh in heads:
+        e_o, e_l, tol = _compare(out[bh[0]:bh[0] + 1, bh[1]:bh[1] + 1], lse[bh[0]:bh[0] + 1, bh[1]:bh[1] + 1],
+                                 deq["Q"][bh][None, None], deq["K"][bh][None, None], deq["V"][bh][None, None],
+                                 qpos, local, [(0, 0)], scale, segs)
+        assert e_o <= tol and e_l <= LSE_TOL, (bh, e_o, tol, e_l)
+
+
 def test_fp8_ring_full_share_256_row_blocks():
     """The bench's configuration: rank 0 of the 32K cp=8 share with all 32 heads, where every launch's grid
     fills the chip with 256-row workgroups (the small-head cases above run 128-row ones).  Sampled rows of
