@@ -110,9 +110,11 @@ RING_CASES = [
 ] + [
     ("s8k_cp2", r, None) for r in range(2)
 ] + [
-    ("s16k_cp4", r, 256) for r in range(4)
+    ("s16k_cp4", 0, None)    # rank 0: every row of every head
 ] + [
-    ("s32k_cp8", 0, 128), ("s32k_cp8", 7, 128),
+    ("s16k_cp4", r, 256) for r in range(1, 4)
+] + [
+    ("s32k_cp8", 0, None), ("s32k_cp8", 7, 128),
     ("s64k_cp16", 0, 512),
 ]
 
