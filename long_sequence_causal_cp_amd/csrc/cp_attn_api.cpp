@@ -653,8 +653,6 @@ cp_status_t ring_fwd(const void* q, const cp_chunks_t* q_chunks, const void* con
   float* part_lse = reinterpret_cast<float*>(p);
   p += round256(2 * R * 4);
   unsigned* part_cnt = reinterpret_cast<unsigned*>(p);
-  hipError_t e0 = cpattn::launch_zero_u32(part_cnt, kSplitMaxBlocks, stream);
-  if (e0 != hipSuccess) return hip_fail(e0, "counter fill launch");
   st = ring_replay(q_chunks, k_steps, v_steps, kv_chunks_steps, n_steps, steps_per_launch, kv_bytes, ws, stream,
                    copy_stream,
                    [&](const RingLaunch& rl) -> hipError_t {
@@ -665,6 +663,8 @@ cp_status_t ring_fwd(const void* q, const cp_chunks_t* q_chunks, const void* con
                        a.part_lse = part_lse;
                        a.part_cnt = part_cnt;
                        a.part_rows = (int)R;
+                       // the ring's first launch clears the key-split counters
+                       a.cnt_to_clear = rl.first_step == 0 ? part_cnt : nullptr;
                        for (int i = 1; i < rl.count; ++i)
                          add_kv_block(a, rl.k[i], rl.v[i], &kv_chunks_steps[rl.first_step + i]);
                        for (int c : rl.active) a.flags[c] = rl.flags[c] | cpattn::kFlagLaneO;

@@ -51,6 +51,11 @@ struct StepArgs {
   float* part_lse;
   unsigned* part_cnt;
   int part_rows;              // capacity in rows; 0: no key split
+  // Non-null: the kSplitMaxBlocks counters still hold the caller's garbage.
+  // An unsplit launch clears them from its first workgroup (stream order
+  // makes that visible to later launches); a split launch clears them with
+  // a small kernel before it starts.
+  unsigned* cnt_to_clear;
 };
 
 // Rows of the key-split partial buffers a ring workspace holds: a launch

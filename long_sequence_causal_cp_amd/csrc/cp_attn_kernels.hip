@@ -88,6 +88,11 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   const int g = lane >> 5;
   const int lq = lane & 31;
 
+  if constexpr (!kSplit) {
+    if (a.cnt_to_clear != nullptr && blockIdx.x == 0)
+      for (int i = threadIdx.x; i < kSplitMaxBlocks; i += blockDim.x) a.cnt_to_clear[i] = 0u;
+  }
+
   // ---- which (row block, batch*head) this workgroup owns ----
   // With a key split (kSplit) two workgroups share a row block, each over
   // half of its key tiles; `ks` says which half.  The pair keeps the same
@@ -729,7 +734,8 @@ hipError_t launch_step(const StepArgs& args, int D, hipStream_t stream, const ch
   a.rb_per_chunk = a.q_chunk_len / bm;
   const long long grid = (long long)a.n_order * a.rb_per_chunk * a.BH;
   if (name) *name = nullptr;
-  if (grid <= 0) return hipSuccess;
+  if (grid <= 0)  // nothing to launch; counters this launch was to clear are cleared all the same
+    return a.cnt_to_clear != nullptr ? launch_zero_u32(a.cnt_to_clear, kSplitMaxBlocks, stream) : hipSuccess;
   if (bm == 128 && grid < 2LL * device_cus() && grid <= kSplitMaxBlocks && split_fits(grid * 128)) split = true;
   // Heads per group: the most heads (a divisor of an XCD's share) whose row
   // blocks fit in what one XCD runs at once (one 256-row or two 128-row
@@ -742,6 +748,11 @@ hipError_t launch_step(const StepArgs& args, int D, hipStream_t stream, const ch
     const long long rb_per_head = (long long)a.n_order * a.rb_per_chunk * (split ? 2 : 1);
     const long long slots = (long long)(device_cus() / 8) * (bm == 256 ? 1 : 2) * (diag ? 2 : 1);
     a.heads_per_group = heads_per_group(a.heads_per_xcd, rb_per_head, slots);
+  }
+  if (split && a.cnt_to_clear != nullptr) {
+    const hipError_t e = launch_zero_u32(a.cnt_to_clear, kSplitMaxBlocks, stream);
+    if (e != hipSuccess) return e;
+    a.cnt_to_clear = nullptr;
   }
   const dim3 g((unsigned)(split ? 2 * grid : grid)), blk((unsigned)(2 * bm));  // one wave per 32 rows
   const char* n;
