@@ -101,16 +101,6 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** na
 hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, float* delta, int64_t rows, int D,
                             hipStream_t stream);
 
-// Heads per group of the XCD-aware job order: the most heads (a divisor of
-// heads_per_xcd) whose blocks_per_head workgroups each fit in `slots`, the
-// workgroups one XCD runs at once; at least 1.
-inline int heads_per_group(int heads_per_xcd, long long blocks_per_head, long long slots) {
-  int hpg = 1;
-  for (int d = 1; d <= heads_per_xcd; ++d)
-    if (heads_per_xcd % d == 0 && d * blocks_per_head <= slots) hpg = d;
-  return hpg;
-}
-
 // Row-block height (queries per workgroup) the step kernel uses for a chunk length.
 int step_block_rows(int q_chunk_len);
 

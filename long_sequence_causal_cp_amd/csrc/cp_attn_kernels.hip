@@ -98,15 +98,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a) {
   // half of its key tiles; `ks` says which half.  The pair keeps the same
   // job number modulo 8, so both halves run on one XCD.
   int job = blockIdx.x, ks = 0;
-  if constexpr (kSplit) {
-    if (a.heads_per_xcd > 0) {
-      ks = (job >> 3) & 1;
-      job = (job & 7) | ((job >> 4) << 3);
-    } else {
-      ks = job & 1;
-      job >>= 1;
-    }
-  }
+  if constexpr (kSplit) split_job(blockIdx.x, a.heads_per_xcd, job, ks);
   // the row block's index (heaviest first, see below) and (b, h)
   int rb_idx, bh;
   xcd_job(job, a.BH, a.heads_per_xcd, a.heads_per_group, a.n_order * a.rb_per_chunk, rb_idx, bh);

@@ -7,6 +7,8 @@
 
 #include <stdint.h>
 
+#include "cp_job_map.h"
+
 namespace cpattn {
 namespace {
 
@@ -18,27 +20,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-
-// Which (block, b*h) a workgroup owns.  Workgroups are dealt to the 8 XCDs
-// round-robin.  With heads_per_xcd > 0 (B*H a multiple of 8) each (b, h)
-// stays on one XCD, so that its tiles are shared through that XCD's L2, and
-// an XCD's heads are taken in groups of heads_per_group (a divisor of
-// heads_per_xcd) whose blocks run together; inside a group blocks go in
-// index order, the group's heads interleaved.  Otherwise (b, h) is the
-// fastest-varying index.
-__device__ __forceinline__ void xcd_job(int job, int BH, int heads_per_xcd, int heads_per_group,
-                                        int blocks_per_head, int& blk, int& bh) {
-  if (heads_per_xcd > 0) {
-    const int x = job & 7, kk = job >> 3;
-    const int per_group = heads_per_group * blocks_per_head;
-    const int grp = kk / per_group, in_grp = kk - grp * per_group;
-    blk = in_grp / heads_per_group;
-    bh = x * heads_per_xcd + grp * heads_per_group + in_grp % heads_per_group;
-  } else {
-    blk = job / BH;
-    bh = job % BH;
-  }
-}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -18,7 +18,11 @@
 //     pages' context-parallel loop: the transfer for a later step may fill a
 //     buffer only after the step that used it is done);
 //   - planted mistakes in copies of a plan (a dropped wait, a record moved,
-//     a slot swapped) are caught by that check.
+//     a slot swapped) are caught by that check;
+//   - the kernels' XCD-aware job order (cp_job_map.h) maps the grid one to
+//     one onto (block, b*h), keeps every (b, h) on one XCD, runs a head
+//     group's blocks in consecutive rounds, and splits a key-split grid into
+//     pairs on one XCD; the head-group size divides an XCD's heads and fits.
 // Exit status 0 when every check passes.
 #include <algorithm>
 #include <cstdint>
@@ -30,6 +34,7 @@
 #include <string>
 #include <vector>
 
+#include "../../long_sequence_causal_cp_amd/csrc/cp_job_map.h"
 #include "../../long_sequence_causal_cp_amd/csrc/cp_ring_plan.h"
 
 using namespace cpplan;
@@ -480,8 +485,67 @@ static void check_tables() {
     }
 }
 
+// ---------------------------------------------------------------- job order
+static void check_job_map() {
+  using cpattn::heads_per_group;
+  using cpattn::split_job;
+  using cpattn::xcd_job;
+  const int bhs[] = {1, 2, 3, 8, 12, 16, 24, 32, 64, 72, 128, 256};
+  const int nrbs[] = {1, 2, 3, 4, 8, 16, 32};
+  const long long slotss[] = {16, 32, 64, 128};
+  for (int BH : bhs)
+    for (int nrb : nrbs)
+      for (long long slots : slotss) {
+        const int hpx = BH % 8 == 0 ? BH / 8 : 0;
+        const int hpg = hpx > 0 ? heads_per_group(hpx, nrb, slots) : 0;
+        if (hpx > 0) {
+          CHECK(hpg >= 1 && hpx % hpg == 0, "heads_per_group %d of %d", hpg, hpx);
+          CHECK(hpg == 1 || hpg * (long long)nrb <= slots, "group of %d heads x %d blocks over %lld", hpg, nrb, slots);
+          for (int d = hpg + 1; d <= hpx; ++d)
+            CHECK(hpx % d != 0 || d * (long long)nrb > slots, "a larger group (%d) fits", d);
+        }
+        const int grid = nrb * BH;
+        std::vector<int> seen(grid, 0), xcd_of(BH, -1);
+        bool ok = true;
+        for (int job = 0; job < grid; ++job) {
+          int blk = -1, bh = -1;
+          xcd_job(job, BH, hpx, hpg, nrb, blk, bh);
+          if (blk < 0 || blk >= nrb || bh < 0 || bh >= BH) {
+            ok = false;
+            break;
+          }
+          ++seen[blk * BH + bh];
+          if (hpx > 0) {
+            if (xcd_of[bh] < 0) xcd_of[bh] = job & 7;
+            ok = ok && xcd_of[bh] == (job & 7);
+            // the heads of a group occupy consecutive jobs of their XCD
+            ok = ok && ((job >> 3) / (hpg * nrb)) == (bh - (job & 7) * hpx) / hpg;
+          }
+        }
+        for (int i = 0; ok && i < grid; ++i) ok = seen[i] == 1;
+        CHECK(ok, "xcd_job BH=%d blocks=%d slots=%lld: not one to one, or a head off its XCD or group", BH, nrb,
+              slots);
+        // key split: the doubled grid pairs up on one job, both halves on one XCD
+        std::vector<int> halves(2 * grid, 0);
+        bool sok = true;
+        for (int w = 0; w < 2 * grid; ++w) {
+          int job = -1, ks = -1;
+          split_job(w, hpx, job, ks);
+          if (job < 0 || job >= grid || ks < 0 || ks > 1) {
+            sok = false;
+            break;
+          }
+          ++halves[2 * job + ks];
+          if (hpx > 0) sok = sok && (w & 7) == (job & 7);
+        }
+        for (int i = 0; sok && i < 2 * grid; ++i) sok = halves[i] == 1;
+        CHECK(sok, "split_job BH=%d blocks=%d: not one to one or halves on different XCDs", BH, nrb);
+      }
+}
+
 int main() {
   check_tables();
+  check_job_map();
   // zigzag rings: every size up to the driver's limit, first, middle and last rank
   for (int N = 1; N <= CP_MAX_STEPS; ++N) {
     std::set<int> ranks = {0, N / 2, N - 1};
