@@ -6,7 +6,9 @@ tests/sanitize/ring_plan_check.cpp with g++ -fsanitize=address,undefined and
 runs it: 1..64 ring steps, 1..8 chunks per table, odd tables, every
 steps-per-launch limit, and a happens-before check of every plan's staging
 slots (the double buffering of [MLM] section 5), including planted ordering
-mistakes that the check must catch.
+mistakes that the check must catch; and the kernels' XCD-aware job order
+(csrc/cp_job_map.h): one to one onto (block, b*h), each head on one XCD,
+key-split pairs on one XCD, head groups of the largest size that fits.
 """
 import os
 import shutil
