@@ -27,9 +27,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 # the translation unit of each measured kernel family and the headers it includes
 KERNEL_SOURCES = tuple(os.path.join(HERE, "csrc", f)
-                       for f in ("cp_attn_kernels.hip", "cp_attn_tile.h", "cp_attn_internal.h"))
+                       for f in ("cp_attn_kernels.hip", "cp_attn_tile.h", "cp_attn_internal.h", "cp_job_map.h"))
 BWD_SOURCES = tuple(os.path.join(HERE, "csrc", f)
-                    for f in ("cp_attn_bwd.hip", "cp_attn_tile.h", "cp_attn_internal.h"))
+                    for f in ("cp_attn_bwd.hip", "cp_attn_tile.h", "cp_attn_internal.h", "cp_job_map.h"))
 
 
 def sources_for(kernel: str):
