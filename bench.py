@@ -716,8 +716,8 @@ def main():
                     help="only run a plain copy of this many MiB --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's rank share only; multi-GPU runs are not part of this "
-              "build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU's rank share only; runs on more than one GPU are not "
+              "supported (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_probe_mib > 0:
