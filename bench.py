@@ -442,7 +442,7 @@ PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA, twice the bf16 figure
 def bench_fp8(args, w, Q, K, V, q_tab, kv_tabs, stream):
     """The rank's share with Q, K, V in e4m3 through cp_ring_attn_fwd_fp8 (the
     ring of the bf16 forward: grouped launches, e4m3 staging copies on a side
-    stream) -- the value.  Beside it, on the same box: the bf16 ring, and the
+    stream) -- the value.  Beside it, on the same GPU: the bf16 ring, and the
     chains of one step launch per ring step in fp8 and bf16 (every step's
     blocks resident, no staging).  Quantisation: power-of-two per-tensor
     scales, codes = RNE(x / scale)."""
@@ -539,7 +539,7 @@ def bench_fp8(args, w, Q, K, V, q_tab, kv_tabs, stream):
     n_launch = len(kern_ms) // args.steps
     achieved = flops / n_launch / (avg * 1e-3) / 1e12
 
-    # the bf16 ring and the bf16 chain of step launches, for comparison (same box)
+    # the bf16 ring and the bf16 chain of step launches, for comparison (same GPU)
     def g16(x, t):
         idx = torch.cat([torch.arange(s0, s0 + t.chunk_len) for s0 in t.starts()])
         return x.index_select(2, idx).contiguous().to(dev)
@@ -871,7 +871,7 @@ def main():
             traffic = None
 
     # parity of the timed forwards' result: every row of every (batch, head)
-    # the cpu_baseline leg computed with the oracle (all heads on a box whose
+    # the cpu_baseline leg computed with the oracle (all heads on a machine whose
     # host finishes them within the budget), else a few rows of head (0, 0)
     cpu, ref = None, {}
     if args.cpu_budget > 0:
